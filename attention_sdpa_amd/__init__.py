@@ -1,0 +1,170 @@
+"""attention_sdpa_amd -- Python binding of libattn.so (include/attn.h).
+
+Argument marshalling only: every step of the attention path runs in the HIP
+kernels of libattn.so.  Tensors are torch tensors on the GPU (torch supplies
+device memory and streams); calls are enqueued on the current torch stream.
+If libattn.so is missing the import of a function raises -- there is no
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libattn.so")
+
+ATTN_OK, ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(6)
+ATTN_F32, ATTN_BF16 = 0, 1
+
+# exported C symbols (kept in sync with include/attn.h by the CPU tests)
+SYMBOLS = ("attn_status_str", "attn_version", "kv_store_slots", "attn_prefill_varlen",
+           "attn_decode_workspace_bytes", "attn_decode_paged")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m attention_sdpa_amd.build` "
+                           "(there is no fallback implementation)")
+    lib = ctypes.CDLL(p)
+    vp, i32p = ctypes.c_void_p, ctypes.c_void_p
+    ci, cf, csz = ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.attn_status_str.argtypes = [ci]
+    lib.attn_status_str.restype = ctypes.c_char_p
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = ci
+    lib.kv_store_slots.argtypes = [vp, vp, vp, vp, i32p, ci, ci, ci, ci, ci, ci, vp]
+    lib.kv_store_slots.restype = ci
+    lib.attn_prefill_varlen.argtypes = [vp, vp, vp, vp, i32p, i32p, ci, ci, ci, ci, ci, ci, ci, ci,
+                                        cf, ci, i32p, ci, ci, ci, ci, ci, vp]
+    lib.attn_prefill_varlen.restype = ci
+    lib.attn_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci, ci]
+    lib.attn_decode_workspace_bytes.restype = csz
+    lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, i32p, i32p, ci, ci, ci, ci, ci, ci, ci, cf,
+                                      ci, ci, ci, vp, csz, vp]
+    lib.attn_decode_paged.restype = ci
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != ATTN_OK:
+        msg = load_library().attn_status_str(status).decode()
+        raise AttnError(fn, status, msg)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _i32(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if t.dtype != torch.int32:
+        raise TypeError("index tensors must be int32")
+    return _ptr(t)
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def kv_store_slots(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   slot_mapping: torch.Tensor, stream=None) -> None:
+    """Scatter k/v [T, Hkv, d] into caches [num_blocks, block_size, Hkv, d]."""
+    T, hkv, d = k.shape
+    nb, bs = k_cache.shape[0], k_cache.shape[1]
+    if k_cache.shape != v_cache.shape or k.shape != v.shape or tuple(k_cache.shape[2:]) != (hkv, d):
+        raise ValueError("shape mismatch")
+    if slot_mapping.numel() != T or k.dtype != k_cache.dtype:
+        raise ValueError("slot_mapping/dtype mismatch")
+    lib = load_library()
+    _check("kv_store_slots", lib.kv_store_slots(
+        _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _i32(slot_mapping), T, hkv, d, nb, bs,
+        _dt(k), _stream(stream)))
+
+
+def attn_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
+                        max_seqlen_q: int, max_seqlen_k: int, softmax_scale: float,
+                        causal: bool = True, block_table: Optional[torch.Tensor] = None,
+                        out: Optional[torch.Tensor] = None, out_dtype=None, stream=None) -> torch.Tensor:
+    """Varlen prefill.  block_table=None: k/v packed [total_k, Hkv, d];
+    otherwise k/v are the paged caches [num_blocks, block_size, Hkv, d]."""
+    total_q, hq, d = q.shape
+    if out is None:
+        out = torch.empty((total_q, hq, d), dtype=out_dtype or q.dtype, device=q.device)
+    if block_table is None:
+        total_k, hkv = k.shape[0], k.shape[1]
+        mbs = nb = bs = 0
+    else:
+        total_k = 0
+        nb, bs, hkv = k.shape[0], k.shape[1], k.shape[2]
+        mbs = block_table.shape[1]
+    batch = cu_seqlens_q.numel() - 1
+    lib = load_library()
+    _check("attn_prefill_varlen", lib.attn_prefill_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _i32(cu_seqlens_q), _i32(cu_seqlens_k), batch,
+        int(max_seqlen_q), int(max_seqlen_k), total_q, total_k, hq, hkv, d, float(softmax_scale),
+        int(bool(causal)), _i32(block_table), mbs, nb, bs, _dt(q), _dt(out), _stream(stream)))
+    return out
+
+
+def attn_decode_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                                max_blocks_per_seq: int, block_size: int, split_tokens: int = 0) -> int:
+    return int(load_library().attn_decode_workspace_bytes(
+        batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size, split_tokens))
+
+
+def attn_decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      cache_seqlens: torch.Tensor, block_table: torch.Tensor, softmax_scale: float,
+                      split_tokens: int = 0, workspace: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None, out_dtype=None, stream=None) -> torch.Tensor:
+    """Single-token decode; q [B, Hq, d], caches [num_blocks, block_size, Hkv, d]."""
+    B, hq, d = q.shape
+    nb, bs, hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    mbs = block_table.shape[1]
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=out_dtype or q.dtype, device=q.device)
+    need = attn_decode_workspace_bytes(B, hq, hkv, d, mbs, bs, split_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    lib = load_library()
+    _check("attn_decode_paged", lib.attn_decode_paged(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _i32(cache_seqlens), _i32(block_table),
+        B, hq, hkv, d, mbs, nb, bs, float(softmax_scale), int(split_tokens), _dt(q), _dt(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out

@@ -1,0 +1,210 @@
+// attn_abi.cpp -- the C ABI of libattn.so (declared in include/attn.h).
+//
+// Every entry point validates its host-side arguments first and returns a
+// status without touching the HIP runtime when they are invalid; only then
+// does it configure and launch the kernels on the caller's stream.  Nothing
+// here allocates, synchronises or keeps state between calls.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/attn.h"
+#include "launch.h"
+
+#define ATTN_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int dtype_size(int dt) { return dt == ATTN_F32 ? 4 : (dt == ATTN_BF16 ? 2 : 0); }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+// Split size of the decode key range: the caller's (a positive multiple of
+// 64), or, for 0, one that gives the launch a few thousand workgroups.
+int resolve_split(int batch, int num_kv_heads, int max_blocks_per_seq, int block_size, int split) {
+    if (split < 0 || split % 64 != 0) return -1;
+    if (split > 0) return split;
+    const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
+    const int64_t units = (int64_t)batch * num_kv_heads;
+    const int64_t want_splits = (4096 + units - 1) / units;
+    int64_t s = (cap + want_splits - 1) / want_splits;
+    s = ((s + 255) / 256) * 256;
+    if (s < 256) s = 256;
+    if (s > cap) s = ((cap + 63) / 64) * 64;
+    return (int)s;
+}
+
+struct DecodeLayout {
+    int split;
+    int max_splits;
+    size_t o_bytes;   // ws_o
+    size_t ml_off;    // ws_ml offset (256-aligned)
+    size_t total;
+};
+
+bool decode_layout(int batch, int hq, int hkv, int d, int mbs, int bs, int split_req,
+                   DecodeLayout *L) {
+    if (batch <= 0 || hq <= 0 || hkv <= 0 || d <= 0 || mbs <= 0 || bs <= 0) return false;
+    const int split = resolve_split(batch, hkv, mbs, bs, split_req);
+    if (split <= 0) return false;
+    const int64_t cap = (int64_t)mbs * bs;
+    const int64_t ns = (cap + split - 1) / split;
+    const size_t rows = (size_t)batch * hq * (size_t)ns;
+    L->split = split;
+    L->max_splits = (int)ns;
+    L->o_bytes = rows * (size_t)d * sizeof(float);
+    L->ml_off = (L->o_bytes + 255) / 256 * 256;
+    L->total = L->ml_off + rows * 2 * sizeof(float);
+    return true;
+}
+
+}  // namespace
+
+ATTN_API const char *attn_status_str(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_NULL: return "a required pointer is NULL";
+        case ATTN_ERR_SHAPE: return "invalid or inconsistent sizes";
+        case ATTN_ERR_UNSUPPORTED: return "unsupported dtype, head_dim, alignment or layout";
+        case ATTN_ERR_WORKSPACE: return "decode workspace missing or too small";
+        case ATTN_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+ATTN_API int attn_version(void) { return kVersion; }
+
+ATTN_API int kv_store_slots(const void *k, const void *v, void *k_cache, void *v_cache,
+                            const int32_t *slot_mapping, int num_tokens, int num_kv_heads,
+                            int head_dim, int num_blocks, int block_size, int dtype,
+                            void *stream) {
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0 || block_size <= 0)
+        return ATTN_ERR_SHAPE;
+    const int es = dtype_size(dtype);
+    if (es == 0) return ATTN_ERR_UNSUPPORTED;
+    if (num_tokens == 0) return ATTN_OK;
+    if (!k || !v || !k_cache || !v_cache || !slot_mapping) return ATTN_ERR_NULL;
+    const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * es;
+    if (row_bytes % 16 != 0 || row_bytes > (1 << 30)) return ATTN_ERR_UNSUPPORTED;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+        return ATTN_ERR_UNSUPPORTED;
+    const int64_t total_chunks = (int64_t)num_tokens * (row_bytes / 16);
+    if ((total_chunks + 255) / 256 > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+    return hip_status(attn::launch_kv_store(k, v, k_cache, v_cache, slot_mapping, num_tokens,
+                                            (int)row_bytes, (int64_t)num_blocks * block_size,
+                                            (hipStream_t)stream));
+}
+
+ATTN_API int attn_prefill_varlen(const void *q, const void *k, const void *v, void *o,
+                                 const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                                 int batch, int max_seqlen_q, int max_seqlen_k,
+                                 int total_q, int total_k,
+                                 int num_q_heads, int num_kv_heads, int head_dim,
+                                 float softmax_scale, int causal,
+                                 const int32_t *block_table, int max_blocks_per_seq,
+                                 int num_blocks, int block_size,
+                                 int in_dtype, int out_dtype, void *stream) {
+    if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_k) return ATTN_ERR_NULL;
+    if (batch <= 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 ||
+        num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+        return ATTN_ERR_SHAPE;
+    if (num_q_heads % num_kv_heads != 0) return ATTN_ERR_SHAPE;
+    if (!std::isfinite(softmax_scale)) return ATTN_ERR_SHAPE;
+    const bool paged = block_table != nullptr;
+    if (paged) {
+        if (max_blocks_per_seq <= 0 || num_blocks <= 0 || block_size <= 0) return ATTN_ERR_SHAPE;
+    } else if (total_k < 0) {
+        return ATTN_ERR_SHAPE;
+    }
+    if (out_dtype != ATTN_F32 && out_dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (in_dtype == ATTN_BF16) {
+        if (head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+        if (paged && block_size % 64 != 0) return ATTN_ERR_UNSUPPORTED;
+    } else if (in_dtype == ATTN_F32) {
+        if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+    } else {
+        return ATTN_ERR_UNSUPPORTED;
+    }
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_UNSUPPORTED;
+    // grid bound: every launch shape derived below must fit a 32-bit grid
+    const int64_t units = ((int64_t)max_seqlen_q + 31) / 32 * batch * num_q_heads;
+    if (units > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+    if (max_seqlen_q == 0 || total_q == 0) return ATTN_OK;
+
+    attn::VarlenArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o;
+    a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
+    a.block_table = block_table;
+    a.batch = batch;
+    a.max_seqlen_q = max_seqlen_q;
+    a.total_q = total_q;
+    a.total_k = paged ? 0 : total_k;
+    a.hq = num_q_heads; a.hkv = num_kv_heads; a.d = head_dim;
+    a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+    a.causal = causal ? 1 : 0;
+    a.max_blocks_per_seq = paged ? max_blocks_per_seq : 0;
+    a.num_blocks = paged ? num_blocks : 0;
+    a.block_size = paged ? block_size : 0;
+    a.out_f32 = out_dtype == ATTN_F32;
+    const hipError_t e = (in_dtype == ATTN_BF16) ? attn::launch_prefill_bf16(a, (hipStream_t)stream)
+                                                 : attn::launch_prefill_f32(a, (hipStream_t)stream);
+    return hip_status(e);
+}
+
+ATTN_API size_t attn_decode_workspace_bytes(int batch, int num_q_heads, int num_kv_heads,
+                                            int head_dim, int max_blocks_per_seq,
+                                            int block_size, int split_tokens) {
+    DecodeLayout L;
+    if (!decode_layout(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size,
+                       split_tokens, &L))
+        return 0;
+    return L.total;
+}
+
+ATTN_API int attn_decode_paged(const void *q, const void *k_cache, const void *v_cache,
+                               void *o, const int32_t *cache_seqlens,
+                               const int32_t *block_table, int batch, int num_q_heads,
+                               int num_kv_heads, int head_dim, int max_blocks_per_seq,
+                               int num_blocks, int block_size, float softmax_scale,
+                               int split_tokens, int in_dtype, int out_dtype,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+    if (!q || !k_cache || !v_cache || !o || !cache_seqlens || !block_table) return ATTN_ERR_NULL;
+    if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        max_blocks_per_seq <= 0 || num_blocks <= 0 || block_size <= 0)
+        return ATTN_ERR_SHAPE;
+    if (num_q_heads % num_kv_heads != 0) return ATTN_ERR_SHAPE;
+    if (!std::isfinite(softmax_scale)) return ATTN_ERR_SHAPE;
+    if (in_dtype != ATTN_BF16 || head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+    if (out_dtype != ATTN_F32 && out_dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (num_q_heads / num_kv_heads > 16) return ATTN_ERR_UNSUPPORTED;
+    if (block_size % 64 != 0) return ATTN_ERR_UNSUPPORTED;
+    if (split_tokens < 0 || split_tokens % 64 != 0) return ATTN_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+        return ATTN_ERR_UNSUPPORTED;
+    DecodeLayout L;
+    if (!decode_layout(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size,
+                       split_tokens, &L))
+        return ATTN_ERR_SHAPE;
+    if ((int64_t)batch * L.max_splits * num_kv_heads > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+    if (!workspace || workspace_bytes < L.total) return ATTN_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_ERR_WORKSPACE;
+
+    attn::DecodeArgs a;
+    a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.o = o;
+    a.cache_seqlens = cache_seqlens; a.block_table = block_table;
+    a.batch = batch; a.hq = num_q_heads; a.hkv = num_kv_heads; a.d = head_dim;
+    a.max_blocks_per_seq = max_blocks_per_seq; a.num_blocks = num_blocks; a.block_size = block_size;
+    a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+    a.split_tokens = L.split;
+    a.max_splits = L.max_splits;
+    a.ws_o = reinterpret_cast<float *>(workspace);
+    a.ws_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + L.ml_off);
+    a.out_f32 = out_dtype == ATTN_F32;
+    return hip_status(attn::launch_decode(a, (hipStream_t)stream));
+}

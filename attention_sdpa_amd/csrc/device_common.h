@@ -1,0 +1,39 @@
+// device_common.h -- small device helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+#define ATTN_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_inff();
+
+// 2^x with the hardware transcendental unit (v_exp_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// Round-to-nearest-even float -> bf16 (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16 f32_to_bf16(float x) { return (bf16)x; }
+
+// Value held by lane (lane ^ 32): exchanges the two 32-lane halves.
+__device__ __forceinline__ float swap_halves(float x) {
+    return __shfl_xor(x, 32, 64);
+}
+
+// 16-byte global load/store helpers.
+__device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ void st16(void *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
+
+}  // namespace attn

@@ -1,0 +1,185 @@
+/*
+ * attn.h -- C ABI of libattn.so: fused scaled-dot-product attention for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operations are those of the blog post "从零实现 vLLM (1.3)：如何加速
+ * Attention 计算": O = softmax(s * Q K^T) V (section Attention 的计算过程,
+ * with the scale of the 标准实现方法 second step), computed in one pass over
+ * K/V tiles with the online-softmax state (m, d', o') of sections
+ * FlashAttention 的最终实现 and 计算流程(1-Pass 算法与分块), so that the logits
+ * and probabilities never reach device memory.  Argument names follow the
+ * calls in the page's Attention 源码分析 section (store_kvcache,
+ * flash_attn_varlen_func, flash_attn_with_kvcache).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every array argument is a DEVICE pointer to a packed, row-major array
+ *   owned by the caller.  The library never allocates, frees or retains
+ *   memory, keeps no global mutable state, and is safe to call from several
+ *   host threads on different streams.
+ * - stream is a hipStream_t passed as void* (NULL = the default stream).
+ *   Calls are asynchronous on that stream and never synchronise the host.
+ * - Host-side argument validation runs before any HIP call.  On failure the
+ *   call returns a nonzero status and launches nothing.  Launch failures
+ *   return ATTN_ERR_HIP.  No C++ exception crosses the ABI.
+ * - Values that live in device memory (cu_seqlens, block tables, slot
+ *   mappings, cache lengths) are preconditions the host cannot check without
+ *   a sync.  The kernels bound every access by the sizes passed here: a
+ *   block id outside [0, num_blocks) reads as a zero row, a slot outside the
+ *   cache is skipped, and a sequence range outside [0, total) is clipped, so
+ *   bad metadata gives wrong numbers, never an out-of-bounds access.
+ * - dtype codes: ATTN_F32 (IEEE binary32) and ATTN_BF16 (bfloat16).
+ * - Grouped-query attention: query head h reads KV head h / (Hq / Hkv).
+ */
+#ifndef ATTN_MI355X_ATTN_H
+#define ATTN_MI355X_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,        /* a required pointer is NULL                    */
+    ATTN_ERR_SHAPE = 2,       /* a size is negative/zero or sizes disagree      */
+    ATTN_ERR_UNSUPPORTED = 3, /* valid, but not a supported dtype/head_dim/... */
+    ATTN_ERR_WORKSPACE = 4,   /* decode workspace missing or too small          */
+    ATTN_ERR_HIP = 5          /* the HIP runtime reported an error              */
+};
+
+enum attn_dtype { ATTN_F32 = 0, ATTN_BF16 = 1 };
+
+/* Status code -> static, human-readable string (never NULL). */
+const char *attn_status_str(int status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int attn_version(void);
+
+/*
+ * kv_store_slots -- the store_kvcache step of the page's Attention 源码分析
+ * section, run before attention in both prefill and decode.
+ *
+ * For every token t in [0, num_tokens) with slot = slot_mapping[t] >= 0:
+ *     k_cache[slot / block_size][slot % block_size][g][:] = k[t][g][:]
+ *     v_cache[slot / block_size][slot % block_size][g][:] = v[t][g][:]
+ * for all KV heads g.  Negative slots are skipped (padding tokens); slots at
+ * or beyond num_blocks * block_size are skipped too.  Bit-exact copy.
+ *
+ *   k, v          [num_tokens, num_kv_heads, head_dim]     dtype, 16-B aligned
+ *   k_cache,
+ *   v_cache       [num_blocks, block_size, num_kv_heads, head_dim], dtype
+ *   slot_mapping  [num_tokens] int32; slots must be distinct (two tokens
+ *                 writing one slot race and the result is either of them)
+ *   dtype         ATTN_BF16 or ATTN_F32
+ * num_tokens == 0 is a no-op returning ATTN_OK.
+ */
+int kv_store_slots(const void *k, const void *v, void *k_cache, void *v_cache,
+                   const int32_t *slot_mapping, int num_tokens, int num_kv_heads,
+                   int head_dim, int num_blocks, int block_size, int dtype,
+                   void *stream);
+
+/*
+ * attn_prefill_varlen -- variable-length prefill (the page's Prefill section,
+ * flash_attn_varlen_func), including the prefix-cache case.
+ *
+ * Sequences are packed without padding.  Sequence b owns query rows
+ * cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (Lq_b of them) and Lk_b =
+ * cu_seqlens_k[b+1] - cu_seqlens_k[b] keys.  For each query row i of
+ * sequence b and query head h:
+ *     O[i][h][:] = sum_{j in J} softmax_j(s * q_i . k_j) v_j
+ * with J = { j < Lk_b : !causal or j <= i + Lk_b - Lq_b }, i.e. the causal
+ * mask is aligned to the END of the sequence, so that with a prefix cache
+ * (Lq_b < Lk_b, queries are the newest tokens) query i sits at absolute
+ * position Lk_b - Lq_b + i.  A row with an empty J is written as zeros.
+ *
+ * K/V source:
+ *   block_table == NULL: k, v are packed [total_k, num_kv_heads, head_dim];
+ *       key j of sequence b is row cu_seqlens_k[b] + j.  max_blocks_per_seq,
+ *       num_blocks and block_size are ignored.
+ *   block_table != NULL (prefix cache): k, v are the paged caches
+ *       [num_blocks, block_size, num_kv_heads, head_dim]; key j of sequence
+ *       b is slot block_table[b * max_blocks_per_seq + j / block_size]
+ *       * block_size + j % block_size.  total_k is ignored; Lk_b still comes
+ *       from cu_seqlens_k.  Table entries past ceil(Lk_b / block_size) are
+ *       never read.
+ *
+ *   q            [total_q, num_q_heads, head_dim], in_dtype
+ *   o            [total_q, num_q_heads, head_dim], out_dtype (written only
+ *                for rows that belong to a sequence)
+ *   cu_seqlens_q, cu_seqlens_k  [batch + 1] int32, nondecreasing, from 0
+ *   max_seqlen_q, max_seqlen_k  upper bounds of Lq_b, Lk_b (host ints; they
+ *                size the launch, rows beyond max_seqlen_q are not computed)
+ *   softmax_scale  s (usually 1/sqrt(head_dim))
+ *   causal       nonzero = causal mask as above
+ *
+ * Supported: in_dtype ATTN_BF16 with head_dim 128 (bf16 matrix cores, fp32
+ * softmax state) and in_dtype ATTN_F32 with head_dim 64 or 128 (fp32
+ * throughout); out_dtype ATTN_F32 or ATTN_BF16 (round to nearest even);
+ * num_q_heads a multiple of num_kv_heads; block_size a multiple of 64 when
+ * paged.  Pointers must be 16-byte aligned.
+ */
+int attn_prefill_varlen(const void *q, const void *k, const void *v, void *o,
+                        const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                        int batch, int max_seqlen_q, int max_seqlen_k,
+                        int total_q, int total_k,
+                        int num_q_heads, int num_kv_heads, int head_dim,
+                        float softmax_scale, int causal,
+                        const int32_t *block_table, int max_blocks_per_seq,
+                        int num_blocks, int block_size,
+                        int in_dtype, int out_dtype, void *stream);
+
+/*
+ * attn_decode_workspace_bytes -- bytes of device workspace attn_decode_paged
+ * needs for these sizes (0 if the sizes are invalid).  split_tokens as in
+ * attn_decode_paged.
+ */
+size_t attn_decode_workspace_bytes(int batch, int num_q_heads, int num_kv_heads,
+                                   int head_dim, int max_blocks_per_seq,
+                                   int block_size, int split_tokens);
+
+/*
+ * attn_decode_paged -- single-token decode against a paged KV cache (the
+ * page's Decode section, flash_attn_with_kvcache with q.unsqueeze(1)).
+ *
+ * For each sequence b and query head h, with L = cache_seqlens[b] (the
+ * context length INCLUDING the token just stored by kv_store_slots):
+ *     O[b][h][:] = sum_{j < L} softmax_j(s * q[b][h] . k_j) v_j
+ * where key j is cache slot block_table[b * max_blocks_per_seq +
+ * j / block_size] * block_size + j % block_size.  With one query per
+ * sequence the causal mask hides nothing.  L == 0 gives a zero row; L is
+ * clipped to max_blocks_per_seq * block_size.
+ *
+ * The key range of each (sequence, KV head) is cut into splits of
+ * split_tokens keys (0 = the library's choice, else a positive multiple of
+ * 64); each split's partial state (m, d', unnormalised o') goes to the
+ * workspace and a second kernel merges the partials with the same
+ * rescaling the online recurrence uses.
+ *
+ *   q             [batch, num_q_heads, head_dim], in_dtype
+ *   k_cache,
+ *   v_cache       [num_blocks, block_size, num_kv_heads, head_dim], in_dtype
+ *   o             [batch, num_q_heads, head_dim], out_dtype
+ *   cache_seqlens [batch] int32
+ *   block_table   [batch, max_blocks_per_seq] int32
+ *   workspace     device scratch of at least attn_decode_workspace_bytes()
+ *                 bytes, 256-byte aligned, not shared with a concurrent call
+ *
+ * Supported: in_dtype ATTN_BF16, head_dim 128, num_q_heads / num_kv_heads
+ * <= 16, block_size a multiple of 64; out_dtype ATTN_F32 or ATTN_BF16.
+ */
+int attn_decode_paged(const void *q, const void *k_cache, const void *v_cache,
+                      void *o, const int32_t *cache_seqlens,
+                      const int32_t *block_table, int batch, int num_q_heads,
+                      int num_kv_heads, int head_dim, int max_blocks_per_seq,
+                      int num_blocks, int block_size, float softmax_scale,
+                      int split_tokens, int in_dtype, int out_dtype,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_MI355X_ATTN_H */

@@ -1,0 +1,97 @@
+"""Shared helpers for the GPU parity tests: device transfer, oracle calls on
+the exact inputs the GPU sees, and the tolerances.
+
+Tolerances (fixed by the accuracy targets of this project):
+* fp32 inputs: max |gpu - oracle| <= 1e-5;
+* bf16 inputs, fp32 output: max abs <= 1e-2 and mean abs <= 1e-3 against the
+  fp64 oracle computed on the same bf16-rounded inputs;
+* bf16 output: against the oracle rounded to bf16, within 1e-2 plus one
+  bf16 ulp of the reference value (both compared values are rounded to bf16,
+  each by up to half an ulp; the rounding alone can exceed 1e-2 for |O| >= 2);
+* KV store and paging: bit-exact.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+
+F32_MAX_ABS = 1e-5
+BF16_MAX_ABS = 1e-2
+BF16_MEAN_ABS = 1e-3
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def np32(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy()
+
+
+def dev(t: torch.Tensor) -> torch.Tensor:
+    return t.contiguous().cuda()
+
+
+def oracle_varlen(vl, rows=None, causal=None) -> np.ndarray:
+    return oracle.attn_varlen(np32(vl.q), np32(vl.k), np32(vl.v), vl.cu_seqlens_q.numpy(),
+                              vl.cu_seqlens_k.numpy(), vl.softmax_scale,
+                              vl.causal if causal is None else causal, rows=rows)
+
+
+def errs(got, ref):
+    d = np.abs(np.asarray(got, dtype=np.float64) - np.asarray(ref, dtype=np.float64))
+    return float(d.max()) if d.size else 0.0, float(d.mean()) if d.size else 0.0
+
+
+def check_f32(got, ref, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    mx, mean = errs(got, ref)
+    log(f"  {what}: fp32 max abs {mx:.3e} mean abs {mean:.3e}")
+    assert mx <= F32_MAX_ABS, f"{what}: max abs {mx:.3e} > {F32_MAX_ABS}"
+
+
+def check_bf16(got, ref, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    mx, mean = errs(got, ref)
+    log(f"  {what}: bf16 max abs {mx:.3e} mean abs {mean:.3e}")
+    assert mx <= BF16_MAX_ABS, f"{what}: max abs {mx:.3e} > {BF16_MAX_ABS}"
+    assert mean <= BF16_MEAN_ABS, f"{what}: mean abs {mean:.3e} > {BF16_MEAN_ABS}"
+
+
+def check_bf16_output(got_bf16: torch.Tensor, ref, what=""):
+    """bf16-valued output vs the oracle rounded to bf16 (RNE)."""
+    ref = np.asarray(ref, dtype=np.float64)
+    ref_b = torch.from_numpy(ref).to(torch.bfloat16).double().numpy()
+    got = got_bf16.detach().double().cpu().numpy()
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    mag = np.maximum(np.abs(ref_b), 2.0 ** -126)
+    ulp = 2.0 ** (np.floor(np.log2(mag)) - 7)       # bf16: 8 significant bits
+    bound = BF16_MAX_ABS + ulp
+    excess = np.abs(got - ref_b) - bound
+    log(f"  {what}: bf16-out max |diff| {np.abs(got - ref_b).max():.3e}, "
+        f"max excess over bound {excess.max():.3e}")
+    assert np.all(excess <= 0), f"{what}: bf16 output outside 1e-2 + 1 ulp"
+
+
+def sample_rows(cu_q: torch.Tensor, hq: int, n: int, seed: int) -> np.ndarray:
+    """Flat (token * hq + head) rows: the first and last token of every
+    sequence for several heads, plus n random rows."""
+    rng = np.random.default_rng(seed)
+    cu = cu_q.tolist()
+    rows = []
+    for b in range(len(cu) - 1):
+        if cu[b + 1] > cu[b]:
+            for t in (cu[b], cu[b + 1] - 1, (cu[b] + cu[b + 1]) // 2):
+                for h in (0, hq // 2, hq - 1):
+                    rows.append(t * hq + h)
+    total = cu[-1]
+    if total > 0:
+        rows.extend((rng.integers(0, total, n) * hq + rng.integers(0, hq, n)).tolist())
+    return np.unique(np.asarray(rows, dtype=np.int64))

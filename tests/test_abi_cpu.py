@@ -1,0 +1,139 @@
+"""The C ABI without a GPU: libattn.so loads, exports exactly the functions
+include/attn.h declares, and rejects invalid arguments with the documented
+status before making any HIP call (so every case here runs on a machine with
+no GPU at all)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import attention_sdpa_amd as attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\**\s*([A-Za-z_]\w*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def exported_functions():
+    out = subprocess.run(["nm", "-D", "--defined-only", attn.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    return sorted(line.split()[2] for line in out.splitlines() if line.split()[1] == "T")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return attn.load_library()
+
+
+def test_exports_match_header(lib):
+    decl = declared_functions()
+    assert decl == sorted(attn.SYMBOLS), decl
+    assert exported_functions() == decl
+    for name in decl:
+        assert hasattr(lib, name)
+
+
+def test_status_strings_and_version(lib):
+    for s in range(6):
+        assert lib.attn_status_str(s)
+    assert lib.attn_status_str(99) == b"unknown status"
+    assert lib.attn_version() == 10000
+
+
+# Fake, non-null "device" pointers: validation must reject the call before
+# anything dereferences them or calls into HIP.
+P = ctypes.c_void_p(0x100000)
+P2 = ctypes.c_void_p(0x200000)
+MIS = ctypes.c_void_p(0x100008)   # 8-byte aligned only
+
+
+def prefill(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, cu_q=P2, cu_k=P2, batch=2, maxq=16, maxk=16, total_q=20,
+             total_k=20, hq=32, hkv=8, d=128, scale=0.088, causal=1, bt=None, mbs=0, nb=0, bs=0,
+             idt=attn.ATTN_BF16, odt=attn.ATTN_F32, stream=None)
+    a.update(kw)
+    return lib.attn_prefill_varlen(a["q"], a["k"], a["v"], a["o"], a["cu_q"], a["cu_k"], a["batch"],
+                                   a["maxq"], a["maxk"], a["total_q"], a["total_k"], a["hq"], a["hkv"],
+                                   a["d"], a["scale"], a["causal"], a["bt"], a["mbs"], a["nb"], a["bs"],
+                                   a["idt"], a["odt"], a["stream"])
+
+
+def test_prefill_validation(lib):
+    E = attn
+    assert prefill(lib, q=None) == E.ATTN_ERR_NULL
+    assert prefill(lib, cu_k=None) == E.ATTN_ERR_NULL
+    assert prefill(lib, batch=0) == E.ATTN_ERR_SHAPE
+    assert prefill(lib, maxq=-1) == E.ATTN_ERR_SHAPE
+    assert prefill(lib, hq=30, hkv=8) == E.ATTN_ERR_SHAPE
+    assert prefill(lib, hkv=0) == E.ATTN_ERR_SHAPE
+    assert prefill(lib, total_k=-1) == E.ATTN_ERR_SHAPE
+    assert prefill(lib, scale=float("nan")) == E.ATTN_ERR_SHAPE
+    assert prefill(lib, d=64) == E.ATTN_ERR_UNSUPPORTED             # bf16 needs d=128
+    assert prefill(lib, d=96, idt=E.ATTN_F32) == E.ATTN_ERR_UNSUPPORTED
+    assert prefill(lib, idt=7) == E.ATTN_ERR_UNSUPPORTED
+    assert prefill(lib, odt=3) == E.ATTN_ERR_UNSUPPORTED
+    assert prefill(lib, q=MIS) == E.ATTN_ERR_UNSUPPORTED
+    assert prefill(lib, bt=P2, mbs=0, nb=4, bs=256) == E.ATTN_ERR_SHAPE
+    assert prefill(lib, bt=P2, mbs=4, nb=4, bs=100) == E.ATTN_ERR_UNSUPPORTED  # bf16 paged: bs % 64
+    # nothing to do: valid arguments with zero query rows return OK without a launch
+    assert prefill(lib, maxq=0) == E.ATTN_OK
+    assert prefill(lib, total_q=0) == E.ATTN_OK
+
+
+def kvstore(lib, **kw):
+    a = dict(k=P, v=P, kc=P, vc=P, slots=P2, T=4, hkv=8, d=128, nb=4, bs=256, dt=attn.ATTN_BF16)
+    a.update(kw)
+    return lib.kv_store_slots(a["k"], a["v"], a["kc"], a["vc"], a["slots"], a["T"], a["hkv"], a["d"],
+                              a["nb"], a["bs"], a["dt"], None)
+
+
+def test_kvstore_validation(lib):
+    E = attn
+    assert kvstore(lib, T=-1) == E.ATTN_ERR_SHAPE
+    assert kvstore(lib, T=0) == E.ATTN_OK            # no-op
+    assert kvstore(lib, T=0, k=None) == E.ATTN_OK    # no-op needs no pointers
+    assert kvstore(lib, slots=None) == E.ATTN_ERR_NULL
+    assert kvstore(lib, nb=0) == E.ATTN_ERR_SHAPE
+    assert kvstore(lib, dt=5) == E.ATTN_ERR_UNSUPPORTED
+    assert kvstore(lib, hkv=1, d=3) == E.ATTN_ERR_UNSUPPORTED   # 6-byte rows
+    assert kvstore(lib, kc=MIS) == E.ATTN_ERR_UNSUPPORTED
+
+
+def decode(lib, **kw):
+    a = dict(q=P, kc=P, vc=P, o=P, sl=P2, bt=P2, B=4, hq=32, hkv=8, d=128, mbs=32, nb=200, bs=256,
+             scale=0.088, split=0, idt=attn.ATTN_BF16, odt=attn.ATTN_F32, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return lib.attn_decode_paged(a["q"], a["kc"], a["vc"], a["o"], a["sl"], a["bt"], a["B"], a["hq"],
+                                 a["hkv"], a["d"], a["mbs"], a["nb"], a["bs"], a["scale"], a["split"],
+                                 a["idt"], a["odt"], a["ws"], a["wsb"], None)
+
+
+def test_decode_validation(lib):
+    E = attn
+    need = lib.attn_decode_workspace_bytes(4, 32, 8, 128, 32, 256, 0)
+    assert need > 0
+    assert lib.attn_decode_workspace_bytes(0, 32, 8, 128, 32, 256, 0) == 0
+    assert lib.attn_decode_workspace_bytes(4, 32, 8, 128, 32, 256, 100) == 0   # not a multiple of 64
+    assert decode(lib, bt=None) == E.ATTN_ERR_NULL
+    assert decode(lib, B=0) == E.ATTN_ERR_SHAPE
+    assert decode(lib, hq=12, hkv=8) == E.ATTN_ERR_SHAPE
+    assert decode(lib, idt=E.ATTN_F32) == E.ATTN_ERR_UNSUPPORTED
+    assert decode(lib, d=64) == E.ATTN_ERR_UNSUPPORTED
+    assert decode(lib, hq=64, hkv=2) == E.ATTN_ERR_UNSUPPORTED   # group of 32 > 16
+    assert decode(lib, bs=96) == E.ATTN_ERR_UNSUPPORTED
+    assert decode(lib, split=100) == E.ATTN_ERR_UNSUPPORTED
+    assert decode(lib, ws=None) == E.ATTN_ERR_WORKSPACE
+    assert decode(lib, wsb=need - 1) == E.ATTN_ERR_WORKSPACE
+    assert decode(lib, ws=MIS) == E.ATTN_ERR_WORKSPACE   # must be 256-byte aligned
+    # split size changes the workspace exactly as the partial layout says
+    w512 = lib.attn_decode_workspace_bytes(4, 32, 8, 128, 32, 256, 512)
+    w1024 = lib.attn_decode_workspace_bytes(4, 32, 8, 128, 32, 256, 1024)
+    assert w512 >= 4 * 32 * 16 * 130 * 4 and w1024 >= 4 * 32 * 8 * 130 * 4 and w512 > w1024

@@ -1,0 +1,110 @@
+"""GPU parity of attn_decode_paged (after kv_store_slots stores the new
+token) against the fp64 oracle, which reads the logical per-sequence K/V,
+never the paged pool.  Pages: blog post "从零实现 vLLM (1.3)：如何加速
+Attention 计算", section Decode."""
+import numpy as np
+import pytest
+import torch
+
+import attention_sdpa_amd as attn
+import oracle
+import workloads
+from tests.golden import load as load_golden
+from tests.helpers import check_bf16, check_bf16_output, dev, log, np32
+
+pytestmark = pytest.mark.gpu
+
+
+def run_decode(dc, split=0, out_dtype=torch.float32):
+    pg = dc.paged
+    kc, vc = dev(pg.k_cache), dev(pg.v_cache)
+    attn.kv_store_slots(dev(pg.k_new), dev(pg.v_new), kc, vc, dev(pg.slot_mapping))
+    out = attn.attn_decode_paged(dev(dc.q), kc, vc, dev(pg.seqlens_k), dev(pg.block_table),
+                                 dc.softmax_scale, split_tokens=split, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_decode(dc):
+    pg = dc.paged
+    return oracle.attn_decode(np32(dc.q), np32(pg.k_logical), np32(pg.v_logical),
+                              pg.cu_seqlens_k.numpy(), dc.softmax_scale)
+
+
+def make_decode(ctx, hq=32, hkv=8, block_size=256, seed=0, mbs=None):
+    """Decode inputs with explicit context lengths."""
+    B = len(ctx)
+    base = workloads.varlen([1] * B, ctx, hq, hkv, 128, torch.bfloat16, seed)
+    mbs = mbs or max(1, max((c + block_size - 1) // block_size for c in ctx))
+    pg = workloads.paged_pool(base.k, base.v, base.cu_seqlens_k, [max(c - 1, 0) for c in ctx],
+                              block_size, seed + 1, spare_blocks=2, max_blocks_per_seq=mbs)
+    return workloads.Decode(base.q.view(B, hq, 128), base.softmax_scale, pg, f"ctx{ctx}")
+
+
+def test_decode_shapes_example():
+    """The Decode section's example shapes: q [2, 32, 128] -> o [2, 32, 128]."""
+    shp = load_golden("decode_shapes.txt")["q_shape"]
+    dc = make_decode([300, 1000], hq=shp[1], hkv=8, seed=1)
+    assert list(dc.q.shape) == shp
+    log("case decode shapes example")
+    got = run_decode(dc)
+    assert list(got.shape) == shp
+    check_bf16(np32(got), oracle_decode(dc), "decode [2,32,128]")
+
+
+@pytest.mark.parametrize("split", [0, 64, 256, 1024])
+def test_decode_ragged_contexts(split):
+    ctx = [1, 2, 63, 64, 65, 255, 256, 257, 1000, 3000]
+    dc = make_decode(ctx, seed=7)
+    log(f"case decode ragged split={split}")
+    check_bf16(np32(run_decode(dc, split)), oracle_decode(dc), f"decode split {split}")
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 1), (12, 4)])
+def test_decode_group_sizes(hq, hkv):
+    dc = make_decode([17, 700, 129], hq=hq, hkv=hkv, block_size=64, seed=hq + hkv)
+    log(f"case decode groups {hq}/{hkv}")
+    check_bf16(np32(run_decode(dc)), oracle_decode(dc), f"decode {hq}/{hkv}")
+
+
+def test_decode_zero_context_and_bf16_output():
+    dc = make_decode([0, 90, 513], seed=3)
+    log("case decode zero ctx + bf16 out")
+    got = run_decode(dc)
+    ref = oracle_decode(dc)
+    assert np.all(np32(got)[0] == 0)
+    check_bf16(np32(got), ref, "decode zero ctx")
+    got_b = run_decode(dc, out_dtype=torch.bfloat16)
+    check_bf16_output(got_b, ref, "decode bf16 out")
+
+
+def test_decode_equals_last_prefill_row():
+    """Decode of the newest token equals the last row of causal prefill over
+    the same context (both on the GPU, through the same paged cache)."""
+    ctx = [150, 600, 64]
+    dc = make_decode(ctx, hq=8, hkv=2, block_size=64, seed=5)
+    dec = np32(run_decode(dc))
+    pg = dc.paged
+    kc, vc = dev(pg.k_cache), dev(pg.v_cache)
+    attn.kv_store_slots(dev(pg.k_new), dev(pg.v_new), kc, vc, dev(pg.slot_mapping))
+    q = torch.zeros(sum(ctx), 8, 128, dtype=torch.bfloat16)
+    cu = pg.cu_seqlens_k
+    for b in range(3):
+        q[cu[b + 1] - 1] = dc.q[b]
+    pre = attn.attn_prefill_varlen(dev(q), kc, vc, dev(cu), dev(cu), max(ctx), max(ctx),
+                                   dc.softmax_scale, True, block_table=dev(pg.block_table),
+                                   out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    last = np32(pre)[[c - 1 for c in cu[1:].tolist()]]
+    log("case decode == last prefill row")
+    check_bf16(dec, last, "decode vs prefill")
+
+
+def test_full_paged_decode_64():
+    dc = workloads.paged_decode()
+    log(f"case {dc.name}")
+    ref = oracle_decode(dc)
+    got = run_decode(dc)
+    check_bf16(np32(got), ref, "decode 64 (all rows)")
+    for split in (256, 2048):
+        check_bf16(np32(run_decode(dc, split)), ref, f"decode 64 split {split}")

@@ -1,0 +1,211 @@
+"""GPU parity of attn_prefill_varlen against the fp64 oracle.
+
+Small cases are compared element by element on every output; the full-size
+workloads are compared on sampled rows the oracle computes one by one, in
+the same launch configuration the benchmark times.  Pages: blog post
+"从零实现 vLLM (1.3)：如何加速 Attention 计算" (sections Prefill, FlashAttention
+的最终实现, 计算流程(1-Pass 算法与分块))."""
+import numpy as np
+import pytest
+import torch
+
+import attention_sdpa_amd as attn
+import oracle
+import workloads
+from tests.helpers import (check_bf16, check_bf16_output, check_f32, dev, log, np32,
+                           oracle_varlen, sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_varlen(vl, out_dtype=torch.float32, causal=None):
+    out = attn.attn_prefill_varlen(dev(vl.q), dev(vl.k), dev(vl.v), dev(vl.cu_seqlens_q),
+                                   dev(vl.cu_seqlens_k), vl.max_seqlen_q, vl.max_seqlen_k,
+                                   vl.softmax_scale, vl.causal if causal is None else causal,
+                                   out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out
+
+
+# ---------------------------------------------------------------- fp32 path
+
+def test_fp32_single_head_L256_d64():
+    vl = workloads.fp32_single_head()
+    log(f"case {vl.name}")
+    got = run_varlen(vl)
+    check_f32(np32(got), oracle_varlen(vl), vl.name)
+
+
+def test_fp32_stress_logits_near_700():
+    vl = workloads.fp32_stress()
+    log(f"case {vl.name}")
+    got = np32(run_varlen(vl))
+    ref = oracle_varlen(vl)
+    check_f32(got, ref, vl.name)
+    # row 2 is the [700, 710, 705] example's weights applied to V rows 0..2
+    w = np.exp(np.array([-10.0, 0.0, -5.0]))
+    w /= w.sum()
+    assert np.max(np.abs(got[2, 0] - w @ np32(vl.v)[:3, 0].astype(np.float64))) <= 1e-5
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp32_varlen_gqa_ragged(d):
+    vl = workloads.varlen([1, 130, 7, 64, 200], [1, 130, 7, 64, 200], 4, 2, d, torch.float32,
+                          seed=5 + d)
+    log(f"case fp32 varlen gqa d={d}")
+    check_f32(np32(run_varlen(vl)), oracle_varlen(vl), f"fp32 d{d}")
+
+
+def test_fp32_prefix_and_noncausal():
+    vl = workloads.varlen([3, 40, 1], [50, 40, 9], 2, 1, 64, torch.float32, seed=8)
+    log("case fp32 Lq<Lk end-aligned")
+    check_f32(np32(run_varlen(vl)), oracle_varlen(vl), "fp32 prefix")
+    vl.causal = False
+    check_f32(np32(run_varlen(vl)), oracle_varlen(vl), "fp32 non-causal")
+
+
+# ---------------------------------------------------------------- bf16 path
+
+RAGGED = [1, 31, 32, 33, 63, 64, 65, 127, 129, 257, 500]
+
+
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (8, 8), (4, 2), (16, 2), (6, 2)])
+def test_bf16_varlen_ragged(hq, hkv):
+    vl = workloads.varlen(RAGGED, RAGGED, hq, hkv, 128, torch.bfloat16, seed=hq * 10 + hkv)
+    log(f"case bf16 varlen ragged hq={hq} hkv={hkv}")
+    check_bf16(np32(run_varlen(vl)), oracle_varlen(vl), f"bf16 ragged {hq}/{hkv}")
+
+
+def test_bf16_output_dtype():
+    vl = workloads.varlen([77, 300, 5], [77, 300, 5], 8, 2, 128, torch.bfloat16, seed=3)
+    log("case bf16 output")
+    got = run_varlen(vl, out_dtype=torch.bfloat16)
+    assert got.dtype == torch.bfloat16
+    check_bf16_output(got, oracle_varlen(vl), "bf16 out")
+
+
+def test_bf16_end_aligned_causal_and_noncausal():
+    lq = [1, 17, 64, 100, 3, 40]
+    lk = [300, 17, 200, 100, 1, 0]   # includes Lq > Lk (rows see no key) and Lk = 0
+    vl = workloads.varlen(lq, lk, 8, 2, 128, torch.bfloat16, seed=4)
+    log("case bf16 Lq<=Lk end-aligned, empty K")
+    got = np32(run_varlen(vl))
+    ref = oracle_varlen(vl)
+    check_bf16(got, ref, "bf16 end-aligned")
+    # rows that see no key are exactly zero
+    cu = vl.cu_seqlens_q.tolist()
+    assert np.all(got[cu[4]:cu[4] + 2] == 0) and np.all(got[cu[5]:cu[6]] == 0)
+    vl.causal = False
+    check_bf16(np32(run_varlen(vl)), oracle_varlen(vl), "bf16 non-causal")
+
+
+def test_bf16_empty_sequences():
+    vl = workloads.varlen([0, 50, 0, 3], [0, 50, 10, 3], 4, 4, 128, torch.bfloat16, seed=6)
+    log("case bf16 empty sequences")
+    check_bf16(np32(run_varlen(vl)), oracle_varlen(vl), "bf16 empty seqs")
+
+
+def test_bf16_one_hot_logits_exact():
+    """Logit gap > 100 after scaling: the output equals V of the target key
+    to bf16 precision of the inputs (weights are 1 and ~e^-100)."""
+    L, d = 70, 128
+    q = torch.zeros(L, 1, d)
+    q[:, 0, 0] = 1.0
+    k = torch.zeros(L, 1, d)
+    k[:, 0, 0] = -64.0
+    k[5, 0, 0] = 64.0
+    g = torch.Generator().manual_seed(2)
+    v = torch.randn(L, 1, d, generator=g)
+    cu = torch.tensor([0, L], dtype=torch.int32)
+    vl = workloads.Varlen(q.bfloat16(), k.bfloat16(), v.bfloat16(), cu, cu.clone(), L, L, 1.0, False)
+    log("case bf16 one-hot")
+    got = np32(run_varlen(vl))
+    assert np.array_equal(got[:, 0], np.broadcast_to(np32(vl.v)[5, 0], (L, d)))
+
+
+# ---------------------------------------------------------------- paged (prefix cache)
+
+def run_prefix(pp, out_dtype=torch.float32, store=True):
+    pg = pp.paged
+    kc, vc = dev(pg.k_cache), dev(pg.v_cache)
+    if store:
+        attn.kv_store_slots(dev(pg.k_new), dev(pg.v_new), kc, vc, dev(pg.slot_mapping))
+    out = attn.attn_prefill_varlen(dev(pp.q), kc, vc, dev(pp.cu_seqlens_q), dev(pg.cu_seqlens_k),
+                                   pp.max_seqlen_q, pp.max_seqlen_k, pp.softmax_scale, True,
+                                   block_table=dev(pg.block_table), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_prefix(pp, rows=None):
+    pg = pp.paged
+    return oracle.attn_varlen(np32(pp.q), np32(pg.k_logical), np32(pg.v_logical),
+                              pp.cu_seqlens_q.numpy(), pg.cu_seqlens_k.numpy(), pp.softmax_scale,
+                              True, rows=rows)
+
+
+@pytest.mark.parametrize("block_size", [64, 256])
+def test_bf16_prefix_prefill_paged(block_size):
+    pp = workloads.prefix_prefill(n_seqs=6, q_lo=1, q_hi=150, p_lo=0, p_hi=700, hq=8, hkv=2,
+                                  block_size=block_size, seed=21 + block_size)
+    log(f"case bf16 prefix paged bs={block_size}")
+    check_bf16(np32(run_prefix(pp)), oracle_prefix(pp), f"prefix bs{block_size}")
+
+
+def test_paged_block_permutation_bit_identical():
+    """The same logical K/V laid out in two differently permuted pools gives
+    bit-identical outputs (arithmetic order depends on logical positions only),
+    and an identity block table equals the contiguous path bit for bit."""
+    base = workloads.varlen([40, 300, 129], [300, 300, 500], 8, 2, 128, torch.bfloat16, seed=9)
+    outs = []
+    for seed in (1, 2):
+        pg = workloads.paged_pool(base.k, base.v, base.cu_seqlens_k, [0, 0, 0], 64, seed=seed,
+                                  spare_blocks=5)
+        pp = workloads.PrefixPrefill(base.q, base.cu_seqlens_q, base.max_seqlen_q, base.max_seqlen_k,
+                                     base.softmax_scale, pg)
+        outs.append(run_prefix(pp))
+    log("case permutation invariance")
+    assert torch.equal(outs[0], outs[1])
+    contiguous = run_varlen(base)
+    assert torch.equal(outs[0], contiguous)
+
+
+def test_fp32_paged_matches_oracle():
+    base = workloads.varlen([5, 70], [90, 70], 2, 2, 64, torch.float32, seed=10)
+    pg = workloads.paged_pool(base.k, base.v, base.cu_seqlens_k, [80, 0], 16, seed=3)
+    pp = workloads.PrefixPrefill(base.q, base.cu_seqlens_q, base.max_seqlen_q, base.max_seqlen_k,
+                                 base.softmax_scale, pg)
+    log("case fp32 paged")
+    check_f32(np32(run_prefix(pp)), oracle_prefix(pp), "fp32 paged")
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+def test_full_varlen_prefill_16_seqs():
+    vl = workloads.varlen_prefill()
+    log(f"case {vl.name} total_q={vl.q.shape[0]}")
+    got = run_varlen(vl)
+    rows = sample_rows(vl.cu_seqlens_q, 32, 600, seed=1)
+    g = np32(got).reshape(-1, 128)[rows]
+    check_bf16(g, oracle_varlen(vl, rows=rows), "varlen 16 seqs (sampled)")
+    assert torch.isfinite(got).all().item()
+
+
+def test_full_long_prefill_32k():
+    vl = workloads.long_prefill()
+    log(f"case {vl.name}")
+    got = run_varlen(vl)
+    rows = sample_rows(vl.cu_seqlens_q, 32, 300, seed=2)
+    g = np32(got).reshape(-1, 128)[rows]
+    check_bf16(g, oracle_varlen(vl, rows=rows), "long 32k (sampled)")
+    assert torch.isfinite(got).all().item()
+
+
+def test_full_prefix_prefill_32_seqs():
+    pp = workloads.prefix_prefill()
+    log(f"case {pp.name}")
+    got = run_prefix(pp)
+    rows = sample_rows(pp.cu_seqlens_q, 32, 600, seed=3)
+    g = np32(got).reshape(-1, 128)[rows]
+    check_bf16(g, oracle_prefix(pp, rows=rows), "prefix 32 seqs (sampled)")
+    assert torch.isfinite(got).all().item()

@@ -41,7 +41,11 @@ def _gen(seed: int) -> torch.Generator:
 
 
 def _randn(g, shape, std, dtype):
-    x = torch.randn(*shape, generator=g, dtype=torch.float32)
+    # drawn as one flat vector, then viewed with the requested shape
+    n = 1
+    for s in shape:
+        n *= int(s)
+    x = torch.randn(n, generator=g, dtype=torch.float32).view(*shape)
     if std != 1.0:
         x = x * std
     return x.to(dtype)
@@ -194,12 +198,12 @@ def fp32_stress(L=256, d=64, seed=1001) -> Varlen:
     g = _gen(seed + 500)
     q = torch.zeros(L, 1, d, dtype=torch.float32)
     q[:, 0, 0] = 8.0
-    k = torch.randn(L, 1, d, generator=g, dtype=torch.float32)
+    k = _randn(g, (L, 1, d), 1.0, torch.float32)
     delta = torch.round(torch.randn(L, generator=g, dtype=torch.float32) * 5.0 * 256.0) / 256.0
     col = 700.0 + delta
     col[0], col[1], col[2] = 700.0, 710.0, 705.0
     k[:, 0, 0] = col
-    v = torch.randn(L, 1, d, generator=g, dtype=torch.float32)
+    v = _randn(g, (L, 1, d), 1.0, torch.float32)
     cu = _cumsum0([L])
     return Varlen(q, k, v, cu, cu.clone(), L, L, 1.0 / 8.0, True, "fp32_stress_L256_d64")
 
