@@ -1,0 +1,323 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one pass of the Attention layer's forward over one batch of
+synthetic input, as the blog post "从零实现 vLLM (1.3)：如何加速 Attention 计算"
+walks through it (section Attention 源码分析): store the batch's new K/V into
+the paged cache (kv_store_slots), then attention.
+
+* Headline (value): varlen causal prefill, 16 sequences with lengths uniform
+  in [128, 4096] (Lq = Lk), 32 query / 8 KV heads, head_dim 128, bf16 inputs,
+  bf16 output.  value = algorithmic attention flops of the step / step time,
+  in TFLOP/s; algorithmic flops = 4 * d * Hq * (number of visible
+  query-key pairs).  Inputs are resident in HBM before timing starts.
+* decode (extra object): paged decode, batch 64, contexts uniform in
+  [512, 8192], block 256, new token stored first; algorithmic bytes = every
+  cached K and V byte read once per KV head; GB/s.
+* roofline: the prefill kernel alone, from events recorded around each of
+  its launches inside the timed region, against bf16 dense MFMA peak.
+* cpu_baseline: the fp64 CPU oracle timed on a bounded sample of the same
+  workload's rows on this host's cores, scaled to TFLOP/s by the same
+  algorithmic flop count.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+# Sources whose hash identifies each kernel; a recorded HBM-traffic figure is
+# reported only while these files are unchanged since the counters were taken.
+KERNEL_SOURCES = {
+    "prefill": ["attention_sdpa_amd/csrc/prefill_bf16.hip", "attention_sdpa_amd/csrc/device_common.h",
+                "attention_sdpa_amd/csrc/launch.h"],
+    "decode": ["attention_sdpa_amd/csrc/decode.hip", "attention_sdpa_amd/csrc/device_common.h",
+               "attention_sdpa_amd/csrc/launch.h"],
+}
+TRAFFIC_FILES = {"prefill": "profiles/prefill_bf16_varlen16_pmc.md",
+                 "decode": "profiles/decode_paged_b64_pmc.md"}
+
+
+def source_sha(which: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[which]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(which: str):
+    """HBM bytes per launch measured by the FETCH_SIZE / WRITE_SIZE passes
+    recorded in profiles/, or None if missing or the kernel changed since."""
+    path = os.path.join(ROOT, TRAFFIC_FILES[which])
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.split(":", 1)[0].strip() in ("kernel_source_sha256",
+                                                                  "traffic_bytes_per_launch"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256") != source_sha(which):
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def visible_pairs(cu_q, cu_k, causal=True) -> int:
+    """Number of (query, key) pairs that the causal, end-aligned mask keeps."""
+    total = 0
+    for b in range(len(cu_q) - 1):
+        lq, lk = cu_q[b + 1] - cu_q[b], cu_k[b + 1] - cu_k[b]
+        if not causal:
+            total += lq * lk
+            continue
+        for_i0 = lk - lq + 1     # visible keys of query 0 (may be <= 0)
+        # sum_{i=0}^{lq-1} clamp(for_i0 + i, 0, lk)
+        for i in range(lq):
+            n = for_i0 + i
+            total += 0 if n <= 0 else (lk if n > lk else n)
+    return total
+
+
+def timed_loop(step, steps, warmup, torch, inner=None):
+    """W untimed steps, then K timed steps between a device sync on both
+    sides.  inner(i) returns (start_event, end_event) pairs recorded around
+    the kernel of interest inside step i."""
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    pairs = []
+    t0 = time.perf_counter()
+    for i in range(steps):
+        p = step(i)
+        if p is not None:
+            pairs.append(p)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [a.elapsed_time(b) for a, b in pairs]
+    return wall, kernel_ms
+
+
+def bench_prefill(args, torch, attn, workloads):
+    vl = workloads.varlen_prefill()
+    cache = workloads.cache_for_varlen(vl, block_size=256, seed=5)
+    q, k, v = vl.q.cuda(), vl.k.cuda(), vl.v.cuda()
+    cu_q, cu_k = vl.cu_seqlens_q.cuda(), vl.cu_seqlens_k.cuda()
+    kc, vc = cache.k_cache.cuda(), cache.v_cache.cuda()
+    slots = cache.slot_mapping.cuda()
+    out = torch.empty_like(q)
+    Ev = torch.cuda.Event
+
+    def step(i):
+        attn.kv_store_slots(k, v, kc, vc, slots)
+        e0, e1 = Ev(enable_timing=True), Ev(enable_timing=True)
+        e0.record()
+        attn.attn_prefill_varlen(q, k, v, cu_q, cu_k, vl.max_seqlen_q, vl.max_seqlen_k,
+                                 vl.softmax_scale, True, out=out)
+        e1.record()
+        return e0, e1
+
+    wall, kms = timed_loop(step, args.steps, args.warmup, torch)
+    pairs = visible_pairs(vl.cu_seqlens_q.tolist(), vl.cu_seqlens_k.tolist())
+    flops = 4.0 * 128 * 32 * pairs
+    ms_step = wall * 1e3 / args.steps
+    k_ms = sum(kms) / len(kms)
+    lens = (vl.cu_seqlens_q[1:] - vl.cu_seqlens_q[:-1]).tolist()
+    return dict(vl=vl, flops=flops, ms_step=ms_step, kernel_ms=k_ms,
+                tflops_step=flops / (ms_step * 1e-3) / 1e12,
+                tflops_kernel=flops / (k_ms * 1e-3) / 1e12,
+                total_tokens=int(vl.q.shape[0]), lens=lens,
+                bytes_alg=2.0 * (q.numel() + k.numel() + v.numel() + out.numel()))
+
+
+def bench_decode(args, torch, attn, workloads):
+    dc = workloads.paged_decode()
+    pg = dc.paged
+    q = dc.q.cuda()
+    kc, vc = pg.k_cache.cuda(), pg.v_cache.cuda()
+    kn, vn, slots = pg.k_new.cuda(), pg.v_new.cuda(), pg.slot_mapping.cuda()
+    sl, bt = pg.seqlens_k.cuda(), pg.block_table.cuda()
+    out = torch.empty_like(q)
+    need = attn.attn_decode_workspace_bytes(q.shape[0], 32, 8, 128, pg.max_blocks_per_seq, 256, 0)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    Ev = torch.cuda.Event
+
+    def step(i):
+        attn.kv_store_slots(kn, vn, kc, vc, slots)
+        e0, e1 = Ev(enable_timing=True), Ev(enable_timing=True)
+        e0.record()
+        attn.attn_decode_paged(q, kc, vc, sl, bt, dc.softmax_scale, workspace=ws, out=out)
+        e1.record()
+        return e0, e1
+
+    wall, kms = timed_loop(step, args.steps, args.warmup, torch)
+    kv_bytes = float(sum(pg.seqlens_k.tolist())) * 8 * 128 * 2 * 2
+    ms_step = wall * 1e3 / args.steps
+    k_ms = sum(kms) / len(kms)
+    return dict(dc=dc, kv_bytes=kv_bytes, ms_step=ms_step, kernel_ms=k_ms,
+                gbs_step=kv_bytes / (ms_step * 1e-3) / 1e9,
+                gbs_kernel=kv_bytes / (k_ms * 1e-3) / 1e9)
+
+
+def host_threads() -> int:
+    """CPU threads this process may use (its affinity mask, capped by
+    OMP_NUM_THREADS when that is set)."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(n, 1)
+
+
+def cpu_baseline_prefill(vl, seconds: float):
+    """Oracle on a bounded, seeded sample of (token, head) rows, time-boxed
+    to about `seconds`; TFLOP/s from the same algorithmic flop count."""
+    import numpy as np
+    import oracle
+    q = vl.q.float().numpy()
+    k = vl.k.float().numpy()
+    v = vl.v.float().numpy()
+    cu_q = vl.cu_seqlens_q.numpy()
+    cu_k = vl.cu_seqlens_k.numpy()
+    hq = q.shape[1]
+    total = q.shape[0] * hq
+    rng = np.random.default_rng(2024)
+    order = rng.permutation(total)
+    threads = host_threads()
+    oracle.attn_varlen(q, k, v, cu_q, cu_k, vl.softmax_scale, True, rows=order[:64], threads=threads)
+    done, flops, t_used, batch = 0, 0.0, 0.0, 256
+    seq_of = np.searchsorted(cu_q, np.arange(q.shape[0]), side="right") - 1
+    while t_used < seconds and done < total:
+        rows = order[done:done + batch]
+        t0 = time.perf_counter()
+        oracle.attn_varlen(q, k, v, cu_q, cu_k, vl.softmax_scale, True, rows=rows, threads=threads)
+        t_used += time.perf_counter() - t0
+        tok = rows // hq
+        b = seq_of[tok]
+        i = tok - cu_q[b]
+        lq, lk = cu_q[b + 1] - cu_q[b], cu_k[b + 1] - cu_k[b]
+        nvis = np.clip(lk - lq + i + 1, 0, lk)
+        flops += float(4.0 * q.shape[2] * nvis.sum())
+        done += rows.size
+        batch = min(batch * 2, 8192)
+    return dict(value=flops / t_used / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+                sample=f"{done} of {total} (token, head) rows drawn at random (seed 2024) from the "
+                       f"varlen prefill workload, fp64 3-pass oracle, {t_used:.1f} s wall")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
+    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain elementwise copy of 1 GiB (read 1 GiB, write 1 GiB), "
+                         "the reference for scaling the FETCH_SIZE / WRITE_SIZE counters")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by KV head or sequence with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_sdpa_amd as attn
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    attn.load_library()
+    torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        n = (1 << 30) // 4
+        x = torch.ones(n, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.mul(x, 1.0, out=y)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "elementwise copy", "bytes_read": 4 * n,
+                          "bytes_written": 4 * n, "launches": 3}), flush=True)
+        return
+
+    res = {}
+    if args.only in ("all", "prefill"):
+        pre = bench_prefill(args, torch, attn, workloads)
+        print(f"[bench] prefill step {pre['ms_step']:.3f} ms, kernel {pre['kernel_ms']:.3f} ms, "
+              f"{pre['tflops_kernel']:.1f} TFLOP/s kernel", file=sys.stderr, flush=True)
+        res["prefill"] = pre
+    if args.only in ("all", "decode"):
+        dec = bench_decode(args, torch, attn, workloads)
+        print(f"[bench] decode step {dec['ms_step']:.3f} ms, kernels {dec['kernel_ms']:.3f} ms, "
+              f"{dec['gbs_kernel']:.0f} GB/s", file=sys.stderr, flush=True)
+        res["decode"] = dec
+
+    line = {
+        "metric": "prefill attn TFLOP/s (% MFMA peak); paged decode KV GB/s (% HBM peak)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded; no dataset or weights involved)",
+    }
+    if "prefill" in res:
+        pre = res["prefill"]
+        line.update({
+            "value": round(pre["tflops_step"], 2), "unit": "TFLOP/s",
+            "ms_per_step": round(pre["ms_step"], 4),
+            "config": {"workload": "varlen causal prefill: 16 sequences, lengths U[128,4096] "
+                                   "(Lq = Lk), packed by cu_seqlens, 32 Q / 8 KV heads, head_dim "
+                                   "128, bf16 in/out, new K/V stored to a 256-token paged cache "
+                                   "first",
+                       "total_tokens": pre["total_tokens"], "algorithmic_flops": pre["flops"],
+                       "step": "kv_store_slots + attn_prefill_varlen"},
+            "roofline": {"bound": "mfma", "achieved": round(pre["tflops_kernel"], 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(pre["tflops_kernel"] / PEAK_BF16_TFLOPS, 4),
+                         "traffic": recorded_traffic("prefill"),
+                         "kernel": "prefill_bf16_kernel<128>",
+                         "kernel_ms": round(pre["kernel_ms"], 4)},
+        })
+    if "decode" in res:
+        dec = res["decode"]
+        dobj = {"workload": "paged decode: batch 64, contexts U[512,8192], block 256, permuted "
+                            "pool, 32 Q / 8 KV heads, head_dim 128, bf16, new token stored first",
+                "metric": "KV GB/s", "value": round(dec["gbs_step"], 1),
+                "ms_per_step": round(dec["ms_step"], 4),
+                "kv_bytes": dec["kv_bytes"],
+                "roofline": {"bound": "hbm", "achieved": round(dec["gbs_kernel"], 1),
+                             "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": round(dec["gbs_kernel"] / PEAK_HBM_GBS, 4),
+                             "traffic": recorded_traffic("decode"),
+                             "kernel": "decode_split_kernel<128> + decode_combine_kernel<128>",
+                             "kernel_ms": round(dec["kernel_ms"], 4)}}
+        if "prefill" in res:
+            line["decode"] = dobj
+        else:
+            line.update({"value": dobj["value"], "unit": "GB/s", "ms_per_step": dobj["ms_per_step"],
+                         "config": {"workload": dobj["workload"]},
+                         "roofline": dobj["roofline"]})
+    if not args.skip_cpu and "prefill" in res:
+        line["cpu_baseline"] = cpu_baseline_prefill(res["prefill"]["vl"], args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
