@@ -39,7 +39,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    # ATTN_LIBRARY names an alternative build (A/B measurements); unset in
+    # normal use, where the in-tree libattn.so is loaded
+    p = path or os.environ.get("ATTN_LIBRARY") or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(f"{p} is missing: build it with `python -m attention_sdpa_amd.build` "
                            "(there is no fallback implementation)")

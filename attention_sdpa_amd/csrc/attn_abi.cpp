@@ -115,7 +115,7 @@ ATTN_API int attn_prefill_varlen(const void *q, const void *k, const void *v, vo
         num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0)
         return ATTN_ERR_SHAPE;
     if (num_q_heads % num_kv_heads != 0) return ATTN_ERR_SHAPE;
-    if (!std::isfinite(softmax_scale)) return ATTN_ERR_SHAPE;
+    if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return ATTN_ERR_SHAPE;
     const bool paged = block_table != nullptr;
     if (paged) {
         if (max_blocks_per_seq <= 0 || num_blocks <= 0 || block_size <= 0) return ATTN_ERR_SHAPE;
@@ -179,7 +179,7 @@ ATTN_API int attn_decode_paged(const void *q, const void *k_cache, const void *v
         max_blocks_per_seq <= 0 || num_blocks <= 0 || block_size <= 0)
         return ATTN_ERR_SHAPE;
     if (num_q_heads % num_kv_heads != 0) return ATTN_ERR_SHAPE;
-    if (!std::isfinite(softmax_scale)) return ATTN_ERR_SHAPE;
+    if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return ATTN_ERR_SHAPE;
     if (in_dtype != ATTN_BF16 || head_dim != 128) return ATTN_ERR_UNSUPPORTED;
     if (out_dtype != ATTN_F32 && out_dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
     if (num_q_heads / num_kv_heads > 16) return ATTN_ERR_UNSUPPORTED;

@@ -51,14 +51,15 @@ decode_split_kernel(DecodeArgs a) {
     const int s = id % a.max_splits;
     const int b = id / a.max_splits;
 
-    int L = a.cache_seqlens[b];
+    int L = ld_meta(a.cache_seqlens, b);
     const int cap = a.max_blocks_per_seq * a.block_size;
     L = L < 0 ? 0 : (L > cap ? cap : L);
     const int kbeg = s * a.split_tokens;
     if (kbeg >= L) return;
     const int kend = min(L, kbeg + a.split_tokens);
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int group = a.hq / a.hkv;
     const int n = lane & 15;            // query column of this lane (head g*group + n)
     const int gq = lane >> 4;           // lane group 0..3
@@ -83,7 +84,7 @@ decode_split_kernel(DecodeArgs a) {
     bf16 *vbuf = sV[w];
 
     for (int c0 = kbeg + w * kChunk; c0 < kend; c0 += kDecWaves * kChunk) {
-        const int blk = a.block_table[(int64_t)b * a.max_blocks_per_seq + c0 / a.block_size];
+        const int blk = ld_meta(a.block_table, (int64_t)b * a.max_blocks_per_seq + c0 / a.block_size);
         const bool bok = blk >= 0 && blk < a.num_blocks;
         const int64_t base = bok ? ((((int64_t)blk * a.block_size + c0 % a.block_size) * a.hkv + g) * D) : 0;
         const int64_t rstride = (int64_t)a.hkv * D;
@@ -230,7 +231,7 @@ decode_combine_kernel(DecodeArgs a) {
     const int bh = blockIdx.x;  // b * hq + h
     const int b = bh / a.hq;
     const int d = threadIdx.x;
-    int L = a.cache_seqlens[b];
+    int L = ld_meta(a.cache_seqlens, b);
     const int cap = a.max_blocks_per_seq * a.block_size;
     L = L < 0 ? 0 : (L > cap ? cap : L);
     const int ns = (L + a.split_tokens - 1) / a.split_tokens;

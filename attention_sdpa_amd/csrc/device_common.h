@@ -7,12 +7,14 @@
 namespace attn {
 
 typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 #define ATTN_LDS __attribute__((address_space(3)))
+#define ATTN_INLINE __attribute__((always_inline))
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
@@ -30,6 +32,13 @@ __device__ __forceinline__ bf16 f32_to_bf16(float x) { return (bf16)x; }
 // Value held by lane (lane ^ 32): exchanges the two 32-lane halves.
 __device__ __forceinline__ float swap_halves(float x) {
     return __shfl_xor(x, 32, 64);
+}
+
+// Read-only int32 metadata (block tables, sequence offsets): read through the
+// constant address space so that uniform indices become scalar loads, which
+// do not wait behind outstanding vector-memory loads.
+__device__ __forceinline__ int32_t ld_meta(const int32_t *p, int64_t i) {
+    return ((const __attribute__((address_space(4))) int32_t *)(p))[i];
 }
 
 // 16-byte global load/store helpers.

@@ -115,7 +115,13 @@ def timed_loop(step, steps, warmup, torch, inner=None):
 
 
 def bench_prefill(args, torch, attn, workloads):
-    vl = workloads.varlen_prefill()
+    if args.prefill_workload == "long":
+        vl = workloads.long_prefill()
+    elif args.prefill_workload == "noncausal":
+        vl = workloads.varlen_prefill()
+        vl.causal = False
+    else:
+        vl = workloads.varlen_prefill()
     cache = workloads.cache_for_varlen(vl, block_size=256, seed=5)
     q, k, v = vl.q.cuda(), vl.k.cuda(), vl.v.cuda()
     cu_q, cu_k = vl.cu_seqlens_q.cuda(), vl.cu_seqlens_k.cuda()
@@ -129,12 +135,12 @@ def bench_prefill(args, torch, attn, workloads):
         e0, e1 = Ev(enable_timing=True), Ev(enable_timing=True)
         e0.record()
         attn.attn_prefill_varlen(q, k, v, cu_q, cu_k, vl.max_seqlen_q, vl.max_seqlen_k,
-                                 vl.softmax_scale, True, out=out)
+                                 vl.softmax_scale, vl.causal, out=out)
         e1.record()
         return e0, e1
 
     wall, kms = timed_loop(step, args.steps, args.warmup, torch)
-    pairs = visible_pairs(vl.cu_seqlens_q.tolist(), vl.cu_seqlens_k.tolist())
+    pairs = visible_pairs(vl.cu_seqlens_q.tolist(), vl.cu_seqlens_k.tolist(), vl.causal)
     flops = 4.0 * 128 * 32 * pairs
     ms_step = wall * 1e3 / args.steps
     k_ms = sum(kms) / len(kms)
@@ -229,6 +235,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
     ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--prefill-workload", choices=["varlen", "long", "noncausal"], default="varlen",
+                    help="prefill workload to time: the varlen 16-sequence batch (headline), the "
+                         "32768-token single sequence, or the varlen batch without the causal mask")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain elementwise copy of 1 GiB (read 1 GiB, write 1 GiB), "
                          "the reference for scaling the FETCH_SIZE / WRITE_SIZE counters")

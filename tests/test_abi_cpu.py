@@ -76,6 +76,7 @@ def test_prefill_validation(lib):
     assert prefill(lib, hkv=0) == E.ATTN_ERR_SHAPE
     assert prefill(lib, total_k=-1) == E.ATTN_ERR_SHAPE
     assert prefill(lib, scale=float("nan")) == E.ATTN_ERR_SHAPE
+    assert prefill(lib, scale=-0.5) == E.ATTN_ERR_SHAPE
     assert prefill(lib, d=64) == E.ATTN_ERR_UNSUPPORTED             # bf16 needs d=128
     assert prefill(lib, d=96, idt=E.ATTN_F32) == E.ATTN_ERR_UNSUPPORTED
     assert prefill(lib, idt=7) == E.ATTN_ERR_UNSUPPORTED
@@ -125,6 +126,7 @@ def test_decode_validation(lib):
     assert decode(lib, bt=None) == E.ATTN_ERR_NULL
     assert decode(lib, B=0) == E.ATTN_ERR_SHAPE
     assert decode(lib, hq=12, hkv=8) == E.ATTN_ERR_SHAPE
+    assert decode(lib, scale=-1.0) == E.ATTN_ERR_SHAPE
     assert decode(lib, idt=E.ATTN_F32) == E.ATTN_ERR_UNSUPPORTED
     assert decode(lib, d=64) == E.ATTN_ERR_UNSUPPORTED
     assert decode(lib, hq=64, hkv=2) == E.ATTN_ERR_UNSUPPORTED   # group of 32 > 16
