@@ -9,10 +9,13 @@
 // in parallel, each one serially over its key tiles.
 //
 // Mapping onto CDNA4:
-// * A workgroup is 8 wavefronts and owns one KV head g, a block of query
-//   positions and the (up to 4) query heads of g's GQA group, so every K/V
-//   tile brought into LDS serves 256 query rows.  Each wavefront owns one
-//   query head and 32 consecutive positions.
+// * Work units are (sequence, block of query positions, KV head g) with the
+//   (up to 4) query heads of g's GQA group, so every K/V tile brought into
+//   LDS serves 256 query rows; each wavefront owns one query head and 32
+//   consecutive positions.  The kernel is persistent: one 8-wavefront
+//   workgroup per CU walks its share of the units (heaviest first), and its
+//   K/V tile stream runs on across unit boundaries, so that a unit costs no
+//   launch, no pipeline fill and no exposed load latency.
 // * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: keys are the M dimension, so
 //   the accumulator puts one query per lane and 16 of its keys in that lane's
 //   registers.  Row max / row sum are then lane-local plus one exchange of the
@@ -81,8 +84,29 @@ constexpr int kSchedValu = 0x0002;
 constexpr int kSchedMfma = 0x0008;
 constexpr int kSchedDsRead = 0x0100;
 
-#define LDS_PTR(p) ((ATTN_LDS void *)(p))
-#define GLOBAL_PTR(p) ((const __attribute__((address_space(1))) void *)(p))
+// Direct global->LDS load of 16 bytes per lane (global_load_lds_dwordx4 with
+// a scalar base address and a per-lane 32-bit offset): lane l's 16 bytes at
+// sbase + voff land at LDS byte address lds + 16*l.  Issued from inline
+// assembly so that the compiler, which cannot tell which ring stage a later
+// LDS read touches, does not wait for every such load before every read;
+// the kernel orders them itself (s_waitcnt vmcnt + s_barrier).  M0 carries
+// the LDS address and is restored afterwards.
+__device__ __forceinline__ void lds_dma16(const void *sbase, uint32_t voff, uint32_t lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(sbase), "s"(lds)
+        : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const ATTN_LDS void *)p;
+}
 
 // All waves' loads of the current stage have landed; nobody still reads the
 // stage about to be refilled.  The empty asm statements keep the compiler
@@ -97,155 +121,502 @@ __device__ __forceinline__ void stage_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-__global__ void __launch_bounds__(kThreads, 1)
-prefill_bf16_kernel(VarlenArgs a, int nqt, int hpw, int head_chunks) {
-    constexpr int KK = kD / 16;         // MFMA k-steps over head_dim
-    constexpr int DB = kD / 32;         // 32-row blocks of d in O^T
-    // three-stage rings; stage s of K is sK[s] (one array per tensor, so that
-    // stage addresses differ from a shared base by constants)
-    __shared__ __align__(16) bf16 sK[3][kTileElems];
-    __shared__ __align__(16) bf16 sV[3][kTileElems];
+// ---- work units and their schedule --------------------------------------
+//
+// A unit is (sequence b, query block qt, head chunk hc, KV head g): the
+// pos_per_wg query positions from qt * pos_per_wg of the hpw query heads
+// (chunk hc of g's GQA group) that read KV head g.  Its cost is its number
+// of K/V tiles, which under the causal mask grows with qt.  Units are put in
+// rows r = 0, 1, ... with qt = nqt-1-r, so heavier rows come first; row r
+// holds, for every sequence with more than qt query blocks (in sequence
+// order), its head_chunks * hkv units, g fastest.  Unit u of that order
+// goes to workgroup snake(u): round u / grid, position u % grid, reversed
+// in odd rounds -- the greedy assignment for rounds of equal-cost units.
+// Every workgroup derives its own list from cu_seqlens_q at start ("listed"
+// schedule).  Where the sizes exceed the tables below, workgroup i instead
+// takes slots i, i + grid, ... of the padded (qt, b, hc, g) slot grid
+// ("strided" schedule), which is correct for any size but less balanced.
 
-    // ---- work unit -------------------------------------------------------
-    int id = blockIdx.x;
-    const int g = id % a.hkv;
-    id /= a.hkv;
-    const int hc = id % head_chunks;
-    id /= head_chunks;
-    const int b = id % a.batch;
-    const int qt = nqt - 1 - id / a.batch;
-    const int pos_per_wg = kRowsPerWave * (kWaves / hpw);
+constexpr int kMaxBatchListed = 1024;   // sequences
+constexpr int kMaxRowsListed = 4096;    // query blocks per sequence
+constexpr int kMaxUnitsListed = 2048;   // units per workgroup
 
-    int64_t q0 = ld_meta(a.cu_q, b), q1 = ld_meta(a.cu_q, b + 1);
-    q0 = q0 < 0 ? 0 : (q0 > a.total_q ? a.total_q : q0);
-    q1 = q1 < q0 ? q0 : (q1 > a.total_q ? a.total_q : q1);
-    const int Lq = (int)(q1 - q0);
-    int64_t k0 = ld_meta(a.cu_k, b), k1 = ld_meta(a.cu_k, b + 1);
-    int Lk;
+struct Geo {
+    int nqt;            // query-position blocks per sequence (upper bound)
+    int hpw;            // query heads per wave column
+    int head_chunks;    // group / hpw
+    int pos_per_wg;     // query positions per unit
+    int lg, lhc, lb;    // strided schedule: log2 of G2, HC2, B2 (powers of
+    int slots;          // two at or above hkv, head_chunks, batch); slot count
+};
+
+// Bounds of sequence b, clamped as the interface promises.
+struct SeqMeta {
+    int q0, Lq, k0, Lk;
+};
+
+__device__ __forceinline__ SeqMeta seq_meta(const VarlenArgs &a, int b) {
+    SeqMeta m;
+    int q0 = ld_meta(a.cu_q, b), q1 = ld_meta(a.cu_q, b + 1);
+    q0 = q0 < 0 ? 0 : (q0 > a.total_q ? (int)a.total_q : q0);
+    q1 = q1 < q0 ? q0 : (q1 > a.total_q ? (int)a.total_q : q1);
+    m.q0 = q0;
+    m.Lq = q1 - q0;
+    int k0 = ld_meta(a.cu_k, b), k1 = ld_meta(a.cu_k, b + 1);
     if (a.block_table) {
         k1 = k1 < k0 ? k0 : k1;
-        const int64_t cap = (int64_t)a.max_blocks_per_seq * a.block_size;
-        Lk = (int)((k1 - k0) > cap ? cap : (k1 - k0));
+        const int cap = a.max_blocks_per_seq * a.block_size;
+        m.Lk = (k1 - k0) > cap ? cap : (k1 - k0);
+        m.k0 = 0;
     } else {
-        k0 = k0 < 0 ? 0 : (k0 > a.total_k ? a.total_k : k0);
-        k1 = k1 < k0 ? k0 : (k1 > a.total_k ? a.total_k : k1);
-        Lk = (int)(k1 - k0);
+        k0 = k0 < 0 ? 0 : (k0 > a.total_k ? (int)a.total_k : k0);
+        k1 = k1 < k0 ? k0 : (k1 > a.total_k ? (int)a.total_k : k1);
+        m.k0 = k0;
+        m.Lk = k1 - k0;
     }
-    const int p0 = qt * pos_per_wg;
-    if (p0 >= Lq) return;
+    return m;
+}
+
+// One work unit (wave-uniform values).
+struct Unit {
+    int k;              // position in this workgroup's schedule
+    int valid;          // 0 once past the last unit
+    int b, g, hc, qt;
+    int q0, k0, Lq, Lk;
+    int p0;             // first query position of the unit
+    int kv_end;         // keys [0, kv_end) are visible to some row of the unit
+    int n_tiles;        // ceil(kv_end / kBN)
+};
+
+__device__ __forceinline__ void unit_bounds(const VarlenArgs &a, const Geo &geo, Unit &u, const SeqMeta &m) {
+    u.q0 = m.q0;
+    u.Lq = m.Lq;
+    u.k0 = m.k0;
+    u.Lk = m.Lk;
+    u.p0 = u.qt * geo.pos_per_wg;
+    const int last = min(u.p0 + geo.pos_per_wg, u.Lq) - 1;
+    u.kv_end = a.causal ? max(0, min(u.Lk, last + (u.Lk - u.Lq) + 1)) : u.Lk;
+    u.n_tiles = (u.kv_end + kBN - 1) / kBN;
+}
+
+// Strided schedule: the first unit at or after slot counter k (with rows;
+// with tiles too if need_tiles).
+__device__ __forceinline__ Unit find_unit_strided(const VarlenArgs &a, const Geo &geo, int k, bool need_tiles) {
+    Unit u;
+    for (;; ++k) {
+        const int slot = (int)blockIdx.x + k * (int)gridDim.x;
+        u.k = k;
+        if (slot >= geo.slots) {
+            u.valid = 0;
+            u.n_tiles = 0;
+            return u;
+        }
+        u.g = slot & ((1 << geo.lg) - 1);
+        u.hc = (slot >> geo.lg) & ((1 << geo.lhc) - 1);
+        u.b = (slot >> (geo.lg + geo.lhc)) & ((1 << geo.lb) - 1);
+        u.qt = geo.nqt - 1 - (slot >> (geo.lg + geo.lhc + geo.lb));
+        if (u.g >= a.hkv || u.hc >= geo.head_chunks || u.b >= a.batch) continue;   // padding
+        const SeqMeta m = seq_meta(a, u.b);
+        if (u.qt * geo.pos_per_wg >= m.Lq) continue;     // no query rows here
+        unit_bounds(a, geo, u, m);
+        if (need_tiles && u.n_tiles == 0) continue;
+        u.valid = 1;
+        return u;
+    }
+}
+
+// Listed schedule: the first list entry at or after k (with tiles if
+// need_tiles).  Entries: (b, qt << 16 | hc << 8 | g); meta: (q0, Lq, k0, Lk).
+__device__ __forceinline__ Unit find_unit_listed(const VarlenArgs &a, const Geo &geo, const int2 *list,
+                                                 const int4 *meta, int n_mine, int k, bool need_tiles) {
+    Unit u;
+    for (;; ++k) {
+        u.k = k;
+        if (k >= n_mine) {
+            u.valid = 0;
+            u.n_tiles = 0;
+            return u;
+        }
+        const int2 e = list[k];
+        u.b = __builtin_amdgcn_readfirstlane(e.x);
+        const int pk = __builtin_amdgcn_readfirstlane(e.y);
+        u.qt = pk >> 16;
+        u.hc = (pk >> 8) & 255;
+        u.g = pk & 255;
+        const int4 mm = meta[u.b];
+        SeqMeta m;
+        m.q0 = __builtin_amdgcn_readfirstlane(mm.x);
+        m.Lq = __builtin_amdgcn_readfirstlane(mm.y);
+        m.k0 = __builtin_amdgcn_readfirstlane(mm.z);
+        m.Lk = __builtin_amdgcn_readfirstlane(mm.w);
+        unit_bounds(a, geo, u, m);
+        if (need_tiles && u.n_tiles == 0) continue;
+        u.valid = 1;
+        return u;
+    }
+}
+
+// The K/V load cursor: the next tile of the tile stream to be loaded.
+struct KvCursor {
+    int k, valid;
+    int t, n_tiles, kv_end, g;
+    int tok;            // contiguous K/V: key row of the tile's first key
+    int bt_row;         // paged: b * max_blocks_per_seq
+    int bt_i;           // paged: block-table index of the tile
+    int in_blk;         // paged: the tile's offset inside its block
+    int blk;            // paged: the tile's block id (validated)
+};
+
+// Per-wave view of a unit: the query head, this lane's query position and
+// its visible-key limit, and the tile counts of this wave's rows.
+struct WaveView {
+    int head;        // query head of this wave
+    int pos;         // this lane's query position in the sequence
+    int lim;         // keys j < lim are visible to this lane's row (0: none)
+    int w_kv_full;   // every row of the wave sees all keys below this
+    int nw;          // tiles with at least one visible key for the wave
+    bool row_valid;
+};
+
+template <bool kListed>
+__global__ void __launch_bounds__(kThreads, 1)
+prefill_bf16_kernel(VarlenArgs a, Geo geo) {
+    constexpr int KK = kD / 16;         // MFMA k-steps over head_dim
+    constexpr int DB = kD / 32;         // 32-row blocks of d in O^T
+    constexpr int kStageBytes = kTileElems * 2;
+    // three-stage rings: stage i of K is sK[i], of V is sV[i]
+    __shared__ __align__(16) bf16 sK[3][kTileElems];
+    __shared__ __align__(16) bf16 sV[3][kTileElems];
+    // listed schedule: per-sequence bounds, row prefix counts, unit list
+    __shared__ int4 sMeta[kListed ? kMaxBatchListed : 1];
+    __shared__ int sRows[kListed ? kMaxRowsListed : 1];
+    __shared__ int2 sList[kListed ? kMaxUnitsListed : 1];
+    __shared__ int sWaveSum[kWaves];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // group A opens each step with its matrix phase.  Waves w and w + 4
+    // share a SIMD and the older wave wins issue ties, so the younger waves
+    // lead: measured, that order costs the pair less.
+    const bool grpA = w >= 4;
     const int group = a.hq / a.hkv;
-    const int head = g * group + hc * hpw + (w % hpw);
-    const int wp0 = p0 + kRowsPerWave * (w / hpw);    // first position of this wave
     const int n = lane & 31;                           // this lane's query
     const int hf = lane >> 5;                          // lane half
-    const int pos = wp0 + n;
-    const bool row_valid = pos < Lq;
-    const int off = Lk - Lq;                           // end-aligned causal offset
-
-    const int last = min(p0 + pos_per_wg, Lq) - 1;
-    const int kv_end = a.causal ? max(0, min(Lk, last + off + 1)) : Lk;
-    const int wlast = min(wp0 + kRowsPerWave, Lq) - 1;
-    const int w_kv_end = (wp0 < Lq) ? (a.causal ? max(0, min(Lk, wlast + off + 1)) : Lk) : 0;
-    const int w_kv_full = a.causal ? max(0, min(Lk, wp0 + off + 1)) : Lk;  // unmasked below this
-    const int lim = row_valid ? (a.causal ? min(Lk, pos + off + 1) : Lk) : 0;
-
-    // ---- Q operand: B[k = d][n = query], 8 consecutive d per lane ---------
-    bf16x8 qf[KK];
-    {
-        const bf16 *qp = (const bf16 *)a.q + ((q0 + (row_valid ? pos : 0)) * a.hq + head) * (int64_t)kD + 8 * hf;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            uint4 t = row_valid ? ld16(qp + 16 * kk) : make_uint4(0, 0, 0, 0);
-            qf[kk] = *reinterpret_cast<bf16x8 *>(&t);
-        }
-    }
-
-    f32x16 o[DB];
-#pragma unroll
-    for (int i = 0; i < DB; ++i) o[i] = f32x16{};
-    float m_ref = kNegInf, mc_ref = 0.f, l_run = 0.f;
     const float cl = a.scale_log2;
-    const bf16x2 ones2 = {(bf16)1.f, (bf16)1.f};
+    const int dr = lane >> 4, dc = lane & 15;
+    const bool paged = a.block_table != nullptr;
+
+    // ---- listed schedule: this workgroup's units --------------------------
+    int n_mine = 0;
+    if constexpr (kListed) {
+        const int nqt = geo.nqt, P = geo.pos_per_wg;
+        const int hcg = geo.head_chunks * a.hkv;
+        for (int b = tid; b < a.batch; b += kThreads) {
+            const SeqMeta m = seq_meta(a, b);
+            sMeta[b] = make_int4(m.q0, m.Lq, m.k0, m.Lk);
+        }
+        for (int r = tid; r < nqt; r += kThreads) sRows[r] = 0;
+        __syncthreads();
+        // sequence b has units in rows r >= nqt - nq_b
+        for (int b = tid; b < a.batch; b += kThreads) {
+            const int nq = min(nqt, (sMeta[b].y + P - 1) / P);
+            if (nq > 0) atomicAdd(&sRows[nqt - nq], 1);
+        }
+        __syncthreads();
+        // two inclusive scans: sequences per row, then sequences in rows <= r
+        constexpr int kPer = kMaxRowsListed / kThreads;
+        for (int pass = 0; pass < 2; ++pass) {
+            int v[kPer];
+            int sum = 0;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int r = tid * kPer + i;
+                sum += (r < nqt) ? sRows[r] : 0;
+                v[i] = sum;
+            }
+            int x = sum;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int y = __shfl_up(x, off, 64);
+                if (lane >= off) x += y;
+            }
+            if (lane == 63) sWaveSum[w] = x;
+            __syncthreads();
+            int excl = x - sum;
+            for (int j = 0; j < w; ++j) excl += sWaveSum[j];
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int r = tid * kPer + i;
+                if (r < nqt) sRows[r] = v[i] + excl;
+            }
+            __syncthreads();
+        }
+        // units in rows < r: hcg * sRows[r - 1]
+        const int grid = (int)gridDim.x, wg = (int)blockIdx.x;
+        const int u_total = hcg * sRows[nqt - 1];
+        const int rounds = u_total / grid, rem = u_total - rounds * grid;
+        n_mine = rounds + ((((rounds & 1) ? grid - 1 - wg : wg) < rem) ? 1 : 0);
+        for (int k = w; k < n_mine; k += kWaves) {
+            const int u = k * grid + ((k & 1) ? grid - 1 - wg : wg);
+            int lo = 0, hi = nqt - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (hcg * __builtin_amdgcn_readfirstlane(sRows[mid - 1]) <= u) lo = mid;
+                else hi = mid - 1;
+            }
+            const int j = u - (lo ? hcg * __builtin_amdgcn_readfirstlane(sRows[lo - 1]) : 0);
+            const int bi = j / hcg, rm = j - bi * hcg;
+            // the bi-th sequence (in index order) present in row lo
+            int seen = 0, bsel = 0;
+            for (int b0 = 0; b0 < a.batch; b0 += 64) {
+                const int b = b0 + lane;
+                bool ok = false;
+                if (b < a.batch) {
+                    const int nq = min(nqt, (sMeta[b].y + P - 1) / P);
+                    ok = nq > 0 && nqt - nq <= lo;
+                }
+                const uint64_t msk = __builtin_amdgcn_ballot_w64(ok);
+                const int c = __builtin_popcountll(msk);
+                if (bi < seen + c) {
+                    const int pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(msk >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)msk, 0));
+                    const uint64_t hit = __builtin_amdgcn_ballot_w64(ok && pre == bi - seen);
+                    bsel = b0 + (int)__builtin_ctzll(hit);
+                    break;
+                }
+                seen += c;
+            }
+            const int qt = nqt - 1 - lo, g = rm % a.hkv, hc = rm / a.hkv;
+            if (lane == 0) sList[k] = make_int2(bsel, (qt << 16) | (hc << 8) | g);
+        }
+        __syncthreads();
+    }
+    auto find_unit = [&](int k, bool need_tiles) ATTN_INLINE {
+        if constexpr (kListed) return find_unit_listed(a, geo, sList, sMeta, n_mine, k, need_tiles);
+        else return find_unit_strided(a, geo, k, need_tiles);
+    };
+
+    auto wave_view = [&](const Unit &u) ATTN_INLINE {
+        WaveView v;
+        v.head = u.g * group + u.hc * geo.hpw + (w % geo.hpw);
+        const int wp0 = u.p0 + kRowsPerWave * (w / geo.hpw);
+        v.pos = wp0 + n;
+        v.row_valid = v.pos < u.Lq;
+        const int off = u.Lk - u.Lq;
+        const int wlast = min(wp0 + kRowsPerWave, u.Lq) - 1;
+        const int w_kv_end = (wp0 < u.Lq) ? (a.causal ? max(0, min(u.Lk, wlast + off + 1)) : u.Lk) : 0;
+        v.w_kv_full = a.causal ? max(0, min(u.Lk, wp0 + off + 1)) : u.Lk;
+        v.lim = v.row_valid ? (a.causal ? min(u.Lk, v.pos + off + 1) : u.Lk) : 0;
+        v.nw = (w_kv_end + kBN - 1) / kBN;
+        return v;
+    };
 
     // ---- direct global -> LDS loads of one K or V tile ---------------------
     // Wave w fills tile rows 8w .. 8w+7 with two 1 KiB loads; lane l lands at
     // physical chunk (l & 15) of row 8w + 4i + (l >> 4) and fetches the
-    // logical chunk that the swizzle puts there.  Rows past the last needed
-    // key repeat that key (finite data; those keys are masked or unused).
-    const int dr = lane >> 4, dc = lane & 15;
-    auto tile_rowbase = [&](int t0) ATTN_INLINE -> int64_t {
-        if (a.block_table) {
-            int blk = ld_meta(a.block_table, (int64_t)b * a.max_blocks_per_seq + t0 / a.block_size);
-            blk = (blk >= 0 && blk < a.num_blocks) ? blk : 0;   // bad id: stay in bounds
-            return (int64_t)blk * a.block_size - t0 + (t0 % a.block_size);
-        }
-        return k0;
-    };
-    auto issue_k = [&](int t, bf16 *dst) ATTN_INLINE {
-        const int t0 = t * kBN;
-        const int64_t base = tile_rowbase(t0);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int r = 8 * w + 4 * i + dr;
-            const int j = min(t0 + r, kv_end - 1);
-            const bf16 *src = (const bf16 *)a.k + ((base + j) * a.hkv + g) * (int64_t)kD + ((dc ^ swz_k(r)) * 8);
-            __builtin_amdgcn_global_load_lds(GLOBAL_PTR(src), LDS_PTR(dst + (8 * w + 4 * i) * kD), 16, 0, 0);
-        }
-    };
-    auto issue_v = [&](int t, bf16 *dst) ATTN_INLINE {
-        const int t0 = t * kBN;
-        const int64_t base = tile_rowbase(t0);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int r = 8 * w + 4 * i + dr;
-            const int j = min(t0 + r, kv_end - 1);
-            const bf16 *src = (const bf16 *)a.v + ((base + j) * a.hkv + g) * (int64_t)kD + ((dc ^ swz_v(r)) * 8);
-            __builtin_amdgcn_global_load_lds(GLOBAL_PTR(src), LDS_PTR(dst + (8 * w + 4 * i) * kD), 16, 0, 0);
-        }
-    };
+    // logical chunk that the swizzle puts there.  Rows past the unit's last
+    // needed key repeat that key (finite data; those keys are masked).
+    const uint32_t k_lds0 = lds_addr(&sK[0][0]) + 8 * w * kD * 2;
+    const uint32_t v_lds0 = lds_addr(&sV[0][0]) + 8 * w * kD * 2;
+    const int r0 = 8 * w + dr, r1 = r0 + 4;            // this lane's tile rows
+    const uint32_t ck0 = (dc ^ swz_k(r0)) * 16, ck1 = (dc ^ swz_k(r1)) * 16;
+    const uint32_t cv0 = (dc ^ swz_v(r0)) * 16, cv1 = (dc ^ swz_v(r1)) * 16;
+    const uint32_t row_bytes = (uint32_t)a.hkv * kD * 2;
+    // offsets of a full tile (no row clamped): no vector ALU work per load
+    const uint32_t fk0 = r0 * row_bytes + ck0, fk1 = r1 * row_bytes + ck1;
+    const uint32_t fv0 = r0 * row_bytes + cv0, fv1 = r1 * row_bytes + cv1;
 
-    // per-lane LDS read offsets (elements)
-    const int k_row = perm23(n);                                   // + 32 per key block
-    const int gq = lane >> 4, s16 = lane & 15;
-    const int v_row_part = 8 * (gq >> 1) + (s16 >> 2);             // + 32kb + 16j (+4 second read)
-    const int v_col_elem = 16 * (gq & 1) + 4 * (s16 & 3);          // + 32*dblk
+    // ---- the K/V tile stream ----------------------------------------------
+    // Stream position s runs over the tiles of this workgroup's units one
+    // after another; its ring stage is s mod 3.  Ring timing (half-steps of
+    // the ping-pong schedule below): K(s) is read in the two matrix
+    // half-steps before step s and refilled with K(s+3) at the barrier
+    // opening the odd half-step of step s; V(s) is read in the two matrix
+    // half-steps of step s and refilled with V(s+3) at the barrier opening
+    // step s+1 (the even half-step, which also waits for K(s+2) and V(s+1)).
+    // V(s) is always issued at the barrier after K(s), from the same rows.
+    Unit C = find_unit(0, false);                          // compute cursor
+    auto skip_empty = [&]() ATTN_INLINE {                  // units with rows but no key: zeros
+        while (C.valid && C.n_tiles == 0) {
+            const WaveView v = wave_view(C);
+            if (v.row_valid) {
+                const int64_t obase = (((int64_t)C.q0 + v.pos) * a.hq + v.head) * (int64_t)kD + 4 * hf;
+#pragma unroll
+                for (int c = 0; c < kD; c += 8) {
+                    if (a.out_f32) *reinterpret_cast<float4 *>((float *)a.o + obase + c) = make_float4(0.f, 0.f, 0.f, 0.f);
+                    else *reinterpret_cast<uint2 *>((bf16 *)a.o + obase + c) = make_uint2(0u, 0u);
+                }
+            }
+            C = find_unit(C.k + 1, false);
+        }
+    };
+    skip_empty();
+    if (!C.valid) return;
 
-    // S^T = K Q^T for a 64-key tile (two 32-key blocks)
-    f32x16 sacc[2];
-    auto qk = [&](const bf16 *Kt) ATTN_INLINE {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            sacc[kb] = f32x16{};
-            const bf16 *krow = Kt + (32 * kb + k_row) * kD;
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                const int ch = (2 * kk + hf) ^ (lane & 15);
-                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(krow + ch * 8);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[kb], 0, 0, 0);
+    auto load_blk = [&](int idx) ATTN_INLINE {
+        const int blk = ld_meta(a.block_table, idx);
+        return (blk >= 0 && blk < a.num_blocks) ? blk : 0;   // bad id: stay in bounds
+    };
+    KvCursor KU;
+    auto cursor_to = [&](const Unit &u) ATTN_INLINE {
+        KU.k = u.k;
+        KU.valid = u.valid;
+        KU.t = 0;
+        KU.n_tiles = u.n_tiles;
+        KU.kv_end = u.kv_end;
+        KU.g = u.g;
+        KU.tok = u.k0;
+        if (paged && u.valid) {
+            KU.bt_row = u.b * a.max_blocks_per_seq;
+            KU.bt_i = 0;
+            KU.in_blk = 0;
+            KU.blk = load_blk(KU.bt_row);
+        }
+    };
+    cursor_to(C);
+    auto advance = [&]() ATTN_INLINE {
+        if (++KU.t >= KU.n_tiles) {
+            cursor_to(find_unit(KU.k + 1, true));
+        } else {
+            KU.tok += kBN;
+            if (paged) {
+                KU.in_blk += kBN;
+                if (KU.in_blk >= a.block_size) {
+                    KU.in_blk = 0;
+                    ++KU.bt_i;
+                    KU.blk = load_blk(KU.bt_row + KU.bt_i);
+                }
             }
         }
-        // issue order: 4 operand reads ahead, then one read per product
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
-#pragma unroll
-        for (int i = 0; i < 12; ++i) {
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     };
-    // O^T += V^T P^T for a 64-key tile, and the row sums from the same bf16
-    // weights
-    bf16x8 pb[4];
-    auto pv = [&](const bf16 *Vt) ATTN_INLINE {
+    int k_stage = 0, v_stage = 0;                          // stage of the next K / V load
+    int last_v = 0, last_k = 0;                            // loads issued at the last even/odd barrier
+    int vq_valid = 0, vq_tok = 0, vq_g = 0, vq_lim = 0;    // the V tile to load next
+    auto issue_k = [&]() ATTN_INLINE {
+        last_k = 0;
+        vq_valid = KU.valid;
+        if (KU.valid) {
+            const int tok = paged ? KU.blk * a.block_size + KU.in_blk : KU.tok;
+            const int lim = min(kBN - 1, KU.kv_end - 1 - KU.t * kBN);
+            const char *src = (const char *)a.k + ((int64_t)tok * a.hkv + KU.g) * (int64_t)(kD * 2);
+            const uint32_t lds = k_lds0 + k_stage * kStageBytes;
+            if (lim == kBN - 1) {
+                lds_dma16(src, fk0, lds);
+                lds_dma16(src, fk1, lds + 4 * kD * 2);
+            } else {
+                lds_dma16(src, (uint32_t)min(r0, lim) * row_bytes + ck0, lds);
+                lds_dma16(src, (uint32_t)min(r1, lim) * row_bytes + ck1, lds + 4 * kD * 2);
+            }
+            vq_tok = tok;
+            vq_g = KU.g;
+            vq_lim = lim;
+            advance();
+            last_k = 2;
+        }
+        k_stage = (k_stage == 2) ? 0 : k_stage + 1;
+    };
+    auto issue_v = [&]() ATTN_INLINE {
+        last_v = 0;
+        if (vq_valid) {
+            const char *src = (const char *)a.v + ((int64_t)vq_tok * a.hkv + vq_g) * (int64_t)(kD * 2);
+            const uint32_t lds = v_lds0 + v_stage * kStageBytes;
+            if (vq_lim == kBN - 1) {
+                lds_dma16(src, fv0, lds);
+                lds_dma16(src, fv1, lds + 4 * kD * 2);
+            } else {
+                lds_dma16(src, (uint32_t)min(r0, vq_lim) * row_bytes + cv0, lds);
+                lds_dma16(src, (uint32_t)min(r1, vq_lim) * row_bytes + cv1, lds + 4 * kD * 2);
+            }
+            last_v = 2;
+        }
+        v_stage = (v_stage == 2) ? 0 : v_stage + 1;
+    };
+    auto even_barrier = [&]() ATTN_INLINE {
+        const int pend = last_v + last_k;
+        if (pend == 4) stage_barrier<kWaitVm4>();
+        else if (pend == 2) stage_barrier<kWaitVm2>();
+        else stage_barrier<kWaitVm0>();
+        issue_v();
+    };
+    auto odd_barrier = [&]() ATTN_INLINE {
+        stage_barrier<kWaitNone>();
+        issue_k();
+    };
+    // stream prologue: K0 V0 K1 V1 K2
+    issue_k();
+    issue_v();
+    issue_k();
+    issue_v();
+    issue_k();
+
+    int st = 0;                                            // ring stage of the unit's first tile
+    bool first = true;
+    for (;;) {
+        // ---- one unit: the ping-pong program on its tiles ----------------
+        const WaveView V = wave_view(C);
+        const int ntl = C.n_tiles;
+        bf16x8 qf[KK];
+        {
+            const bf16 *qp = (const bf16 *)a.q + (((int64_t)C.q0 + (V.row_valid ? V.pos : 0)) * a.hq + V.head) * (int64_t)kD + 8 * hf;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
+            for (int kk = 0; kk < KK; ++kk) {
+                uint4 tq = V.row_valid ? ld16(qp + 16 * kk) : make_uint4(0, 0, 0, 0);
+                qf[kk] = *reinterpret_cast<bf16x8 *>(&tq);
+            }
+        }
+        f32x16 o[DB];
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
+        for (int i = 0; i < DB; ++i) o[i] = f32x16{};
+        float m_ref = kNegInf, mc_ref = 0.f, l_run = 0.f;
+        f32x16 sacc[2];
+        bf16x8 pb[4];
+        const bf16x2 ones2 = {(bf16)1.f, (bf16)1.f};
+        const int k_row = perm23(n);
+        const int gq = lane >> 4, s16 = lane & 15;
+        const int v_row_part = 8 * (gq >> 1) + (s16 >> 2);
+        const int v_col_elem = 16 * (gq & 1) + 4 * (s16 & 3);
+
+        // S^T = K Q^T for a 64-key tile (two 32-key blocks) from K stage ks
+        auto qk = [&](int ks) ATTN_INLINE {
+            const bf16 *Kt = &sK[0][0] + ks * kTileElems;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                sacc[kb] = f32x16{};
+                const bf16 *krow = Kt + (32 * kb + k_row) * kD;
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) {
+                    const int ch = (2 * kk + hf) ^ (lane & 15);
+                    const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(krow + ch * 8);
+                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[kb], 0, 0, 0);
+                }
+            }
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+            for (int i = 0; i < 12; ++i) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        };
+        // One matrix phase: the next tile's S^T = K Q^T from K stage ks and
+        // O^T += V^T P^T for the tile in V stage vs, with the row sums from
+        // the same bf16 weights.  The two products alternate MFMA by MFMA;
+        // the operands of step i + kAhead are read from LDS during step i.
+        auto mma = [&](int ks, int vs) ATTN_INLINE {
+            constexpr int kAhead = 4;
+            const bf16 *Kt = &sK[0][0] + ks * kTileElems;
+            const bf16 *Vt = &sV[0][0] + vs * kTileElems;
+            bf16x8 kbuf[16], vbuf[16];
+            auto read_k = [&](int i) ATTN_INLINE {
+                const int kb = i >> 3, kk = i & 7;
+                const bf16 *krow = Kt + (32 * kb + k_row) * kD;
+                const int ch = (2 * kk + hf) ^ (lane & 15);
+                kbuf[i] = *reinterpret_cast<const bf16x8 *>(krow + ch * 8);
+            };
+            auto read_v = [&](int i) ATTN_INLINE {
+                const int jj = i >> 2, db = i & 3;
                 const int r = 16 * jj + v_row_part;
                 const int col = 32 * db + v_col_elem;
                 const int ch0 = col >> 3, sub = col & 7;
@@ -253,182 +624,184 @@ prefill_bf16_kernel(VarlenArgs a, int nqt, int hpw, int head_chunks) {
                 const bf16 *p1r = Vt + (r + 4) * kD + ((ch0 ^ swz_v(r + 4)) * 8) + sub;
                 const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ATTN_LDS bf16x4 *)(p0r));
                 const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ATTN_LDS bf16x4 *)(p1r));
-                const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[jj], o[db], 0, 0, 0);
-            }
+                vbuf[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            };
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
+            for (int i = 0; i < kAhead; ++i) {
+                read_k(i);
+                read_v(i);
+            }
+            sacc[0] = f32x16{};
+            sacc[1] = f32x16{};
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                sacc[i >> 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kbuf[i], qf[i & 7], sacc[i >> 3], 0, 0, 0);
+                if (i + kAhead < 16) read_k(i + kAhead);
+                const int jj = i >> 2, db = i & 3;
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vbuf[i], pb[jj], o[db], 0, 0, 0);
+                if (i + kAhead < 16) read_v(i + kAhead);
                 bf16x2 pr;
-                pr[0] = pb[jj][2 * e];
-                pr[1] = pb[jj][2 * e + 1];
+                pr[0] = pb[jj][2 * db];
+                pr[1] = pb[jj][2 * db + 1];
                 l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, l_run, false);
+                __builtin_amdgcn_sched_barrier(0);
             }
-        }
-        // issue order: two products' operands ahead, then per product its
-        // next operands and one row-sum step
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+        };
+        // softmax of tile t: mask (diagonal/end tiles only), row max, lazy
+        // reference update (rescaling o', d' if it moves), P = 2^(S c - r c)
+        // in bf16 -- the B operand of the next P V
+        auto softmax = [&](int t) ATTN_INLINE {
+            const int t0 = t * kBN;
+            if (t0 + kBN > V.w_kv_full) {
+                // register i of block kb holds key t0 + 32 kb + 8 hf + c_i,
+                // c_i = i (i < 8) or i + 8; it is masked when key >= lim
 #pragma unroll
-        for (int i = 0; i < 14; ++i) {
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedValu, 1, 0);
-        }
+                for (int kb = 0; kb < 2; ++kb) {
+                    const int thr = V.lim - t0 - 32 * kb - 8 * hf;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedValu, 1, 0);
-        }
-    };
-    // softmax phase of tile t: mask (diagonal/end tiles only), row max, lazy
-    // reference update (rescaling o', d' if it moves), P = 2^(S c - r c) in
-    // bf16 -- the B operand of the next P V
-    auto softmax = [&](int t) ATTN_INLINE {
-        const int t0 = t * kBN;
-        if (t0 + kBN > w_kv_full) {
+                    for (int i = 0; i < 16; ++i)
+                        if ((i < 8 ? i : i + 8) >= thr) sacc[kb][i] = kNegInf;
+                }
+            }
+            float mx = kNegInf;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = t0 + 32 * kb + (i < 8 ? 8 * hf + i : 16 + 8 * hf + (i - 8));
-                    if (key >= lim) sacc[kb][i] = kNegInf;
-                }
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            const bool need = mx > m_ref && (m_ref == kNegInf || mx * cl > mc_ref + kRescaleLog2);
+            if (__builtin_amdgcn_ballot_w64(need)) {
+                const float m_new = fmaxf(m_ref, mx);
+                const float mc_new = (m_new == kNegInf) ? 0.f : m_new * cl;
+                const float alpha = (m_ref == kNegInf) ? 0.f : fast_exp2(mc_ref - mc_new);
+                m_ref = m_new;
+                mc_ref = mc_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+            }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    pb[2 * kb + (i >> 3)][i & 7] = f32_to_bf16(fast_exp2(fmaf(sacc[kb][i], cl, -mc_ref)));
+        };
+
+        auto zero_p = [&]() ATTN_INLINE {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) pb[jj] = bf16x8{};
+        };
+
+        // prologue: K(s0) (and this unit's Q rows) landed.  Waiting for
+        // everything also retires the previous unit's O stores.
+        stage_barrier<kWaitVm0>();                         // half-step -2
+        if (grpA) qk(st);
+        stage_barrier<kWaitNone>();                        // half-step -1
+        if (grpA) {
+            if (V.nw > 0) softmax(0);
+            else zero_p();
+        } else {
+            qk(st);
+            // half-step 0; for later units the V load of this position was
+            // issued at the end of the previous unit
+            if (first) even_barrier();
+            else stage_barrier<kWaitNone>();
+            if (V.nw > 0) softmax(0);
+            else zero_p();
         }
-        float mx = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        const bool need = mx > m_ref && (m_ref == kNegInf || mx * cl > mc_ref + kRescaleLog2);
-        if (__builtin_amdgcn_ballot_w64(need)) {
-            const float m_new = fmaxf(m_ref, mx);
-            const float mc_new = (m_new == kNegInf) ? 0.f : m_new * cl;
-            const float alpha = (m_ref == kNegInf) ? 0.f : fast_exp2(mc_ref - mc_new);
-            m_ref = m_new;
-            mc_ref = mc_new;
-            l_run *= alpha;
+        for (int t = 0; t < ntl; ++t) {
+            const int st1 = (st == 2) ? 0 : st + 1;
+            if (grpA) even_barrier();
+            else odd_barrier();
+            __builtin_amdgcn_s_setprio(1);
+            // every wave runs every step: past its last visible tile its P is
+            // zero (adding exactly 0), and the last step's S^T is unused
+            mma(st1, st);
+            __builtin_amdgcn_s_setprio(0);
+            if (grpA) odd_barrier();
+            else even_barrier();
+            if (t + 1 < V.nw) softmax(t + 1);
+            else zero_p();
+            st = st1;
+        }
+        if (grpA) stage_barrier<kWaitNone>();              // B's last half-step
+
+        // ---- O = o' / d' for this wave's valid rows ----
+        if (V.row_valid) {
+            float l_tot;
+            {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+                l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            }
+            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            const int64_t obase = (((int64_t)C.q0 + V.pos) * a.hq + V.head) * (int64_t)kD;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const int d0 = 32 * db + 8 * a4 + 4 * hf;
+                    const float v0 = o[db][4 * a4] * inv, v1 = o[db][4 * a4 + 1] * inv;
+                    const float v2 = o[db][4 * a4 + 2] * inv, v3 = o[db][4 * a4 + 3] * inv;
+                    if (a.out_f32) {
+                        *reinterpret_cast<float4 *>((float *)a.o + obase + d0) = make_float4(v0, v1, v2, v3);
+                    } else {
+                        bf16x4 r;
+                        r[0] = f32_to_bf16(v0); r[1] = f32_to_bf16(v1);
+                        r[2] = f32_to_bf16(v2); r[3] = f32_to_bf16(v3);
+                        *reinterpret_cast<bf16x4 *>((bf16 *)a.o + obase + d0) = r;
+                    }
+                }
         }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                pb[2 * kb + (i >> 3)][i & 7] = f32_to_bf16(fast_exp2(fmaf(sacc[kb][i], cl, -mc_ref)));
-    };
-
-    // ---- ping-pong schedule ---------------------------------------------
-    // Waves 0-3 (group A) and 4-7 (group B) sit on the four SIMDs in pairs.
-    // Every wave runs the same program -- matrix half-step for tile t
-    // (S(t+1) = K(t+1) Q^T and O += P(t) V(t)), then the vector softmax of
-    // tile t+1 -- but group B runs it one half-step behind group A, so on each
-    // SIMD the matrix core works for one wave while the vector ALU works for
-    // the other.  A barrier separates half-steps.  K and V use three-stage
-    // rings: K(t+3) and V(t+2) are issued at absolute half-step 2t, four
-    // half-steps before their first use, into stages freed at half-step 2t-1.
-    const int n_tiles = (kv_end + kBN - 1) / kBN;        // tiles of the workgroup
-    const int nw = (w_kv_end + kBN - 1) / kBN;           // tiles this wave computes
-    const bool grpA = w < 4;
-    // the barrier opening absolute half-step 2t: tiles K(t+1), V(t) must have
-    // landed (loads of tile t+1's half-steps -- K(t+2), V(t+1) -- may still be
-    // in flight), then the freed stages are refilled
-    auto even_barrier = [&](int t, bf16 *Kf, bf16 *Vf) ATTN_INLINE {
-        const int pend = 2 * (t + 2 < n_tiles) + 2 * (t + 1 < n_tiles);
-        if (pend == 4) stage_barrier<kWaitVm4>();
-        else if (pend == 2) stage_barrier<kWaitVm2>();
-        else stage_barrier<kWaitVm0>();
-        if (t + 3 < n_tiles) issue_k(t + 3, Kf);
-        if (t + 2 < n_tiles) issue_v(t + 2, Vf);
-    };
-    auto mfma_phase = [&](int t, const bf16 *Kn, const bf16 *Vc) ATTN_INLINE {
-        __builtin_amdgcn_s_setprio(1);
-        if (t < nw) {
-            if (t + 1 < nw) qk(Kn);
-            pv(Vc);
-        }
-        __builtin_amdgcn_s_setprio(0);
-    };
-    // prologue: K(0), K(1), V(0), K(2), V(1) in that order
-    if (n_tiles > 0) issue_k(0, sK[0]);
-    if (n_tiles > 1) issue_k(1, sK[1]);
-    if (n_tiles > 0) issue_v(0, sV[0]);
-    if (n_tiles > 2) issue_k(2, sK[2]);
-    if (n_tiles > 1) issue_v(1, sV[1]);
-    {
-        // half-step -2: K(0) landed; everything issued after it may be in flight
-        const int after = (n_tiles > 1 ? 4 : 0) + 2 + (n_tiles > 2 ? 2 : 0);
-        if (after == 8) stage_barrier<kWaitVm8>();
-        else if (after == 6) stage_barrier<kWaitVm6>();
-        else stage_barrier<kWaitVm2>();
+        C = find_unit(C.k + 1, false);
+        skip_empty();
+        if (!C.valid) break;
+        first = false;
     }
-    if (grpA && nw > 0) qk(sK[0]);
-    stage_barrier<kWaitNone>();                          // half-step -1
-    if (grpA) {
-        if (nw > 0) softmax(0);
-    } else {
-        if (nw > 0) qk(sK[0]);
-        even_barrier(0, sK[0], sV[2]);                   // half-step 0
-        if (nw > 0) softmax(0);
-    }
-    // iteration t: A runs half-steps 2t, 2t+1; B runs 2t+1, 2t+2
-    auto iter = [&](int t, const bf16 *Kn, const bf16 *Vc, bf16 *KfA, bf16 *VfA, bf16 *KfB, bf16 *VfB)
-        ATTN_INLINE {
-        if (grpA) even_barrier(t, KfA, VfA);
-        else stage_barrier<kWaitNone>();
-        mfma_phase(t, Kn, Vc);
-        if (grpA) stage_barrier<kWaitNone>();
-        else even_barrier(t + 1, KfB, VfB);
-        if (t + 1 < nw) softmax(t + 1);
-    };
-    for (int t = 0; t < n_tiles; t += 3) {
-        iter(t, sK[1], sV[0], sK[0], sV[2], sK[1], sV[0]);
-        if (t + 1 < n_tiles) iter(t + 1, sK[2], sV[1], sK[1], sV[0], sK[2], sV[1]);
-        if (t + 2 < n_tiles) iter(t + 2, sK[0], sV[2], sK[2], sV[1], sK[0], sV[2]);
-    }
-    if (grpA) stage_barrier<kWaitNone>();                // B's last half-step
-
-    // ---- epilogue: O = o' / d' ----
-    if (!row_valid) return;
-    float l_tot;
-    {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
-        l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    }
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const int64_t obase = ((q0 + pos) * a.hq + head) * (int64_t)kD;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-            const int d0 = 32 * db + 8 * a4 + 4 * hf;
-            const float v0 = o[db][4 * a4] * inv, v1 = o[db][4 * a4 + 1] * inv;
-            const float v2 = o[db][4 * a4 + 2] * inv, v3 = o[db][4 * a4 + 3] * inv;
-            if (a.out_f32) {
-                *reinterpret_cast<float4 *>((float *)a.o + obase + d0) = make_float4(v0, v1, v2, v3);
-            } else {
-                bf16x4 r;
-                r[0] = f32_to_bf16(v0); r[1] = f32_to_bf16(v1);
-                r[2] = f32_to_bf16(v2); r[3] = f32_to_bf16(v3);
-                *reinterpret_cast<bf16x4 *>((bf16 *)a.o + obase + d0) = r;
-            }
-        }
+    // no direct-to-LDS load may outlive the workgroup's LDS allocation
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
 }
 
 }  // namespace
 
 hipError_t launch_prefill_bf16(const VarlenArgs &a, hipStream_t stream) {
     const int group = a.hq / a.hkv;
-    const int hpw = (group % 4 == 0) ? 4 : (group % 2 == 0 ? 2 : 1);
-    const int head_chunks = group / hpw;
-    const int pos_per_wg = kRowsPerWave * (kWaves / hpw);
-    const int nqt = (a.max_seqlen_q + pos_per_wg - 1) / pos_per_wg;
-    const int64_t units = (int64_t)nqt * a.batch * head_chunks * a.hkv;
-    if (units == 0) return hipSuccess;
-    hipLaunchKernelGGL(prefill_bf16_kernel, dim3((unsigned)units), dim3(kThreads), 0, stream,
-                       a, nqt, hpw, head_chunks);
+    Geo geo;
+    geo.hpw = (group % 4 == 0) ? 4 : (group % 2 == 0 ? 2 : 1);
+    geo.head_chunks = group / geo.hpw;
+    geo.pos_per_wg = kRowsPerWave * (kWaves / geo.hpw);
+    geo.nqt = (a.max_seqlen_q + geo.pos_per_wg - 1) / geo.pos_per_wg;
+    auto lg2 = [](int x) { int l = 0; while ((1 << l) < x) ++l; return l; };
+    geo.lg = lg2(a.hkv);
+    geo.lhc = lg2(geo.head_chunks);
+    geo.lb = lg2(a.batch);
+    const int64_t slots = (int64_t)geo.nqt << (geo.lg + geo.lhc + geo.lb);
+    if (slots == 0) return hipSuccess;
+    if (slots > (1LL << 30) || a.total_q > 0x7fffffffLL || a.total_k > 0x7fffffffLL) return hipErrorInvalidValue;
+    geo.slots = (int)slots;
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (cus < 1) cus = 1;
+    // upper bound of the unit count (every sequence at max_seqlen_q)
+    const int64_t units_max = (int64_t)geo.nqt * a.batch * geo.head_chunks * a.hkv;
+    const int64_t grid_l = units_max < cus ? units_max : cus;
+    const bool listed = a.batch <= kMaxBatchListed && geo.nqt <= kMaxRowsListed && a.hkv <= 256 &&
+                        geo.head_chunks <= 256 && (units_max + grid_l - 1) / grid_l <= kMaxUnitsListed;
+    if (listed) {
+        hipLaunchKernelGGL(prefill_bf16_kernel<true>, dim3((unsigned)grid_l), dim3(kThreads), 0, stream, a, geo);
+    } else {
+        // a multiple of the padded KV-head count keeps each workgroup on one head
+        int64_t grid = geo.slots < (int64_t)cus ? geo.slots : (int64_t)cus;
+        const int g2 = 1 << geo.lg;
+        if (grid > g2) grid -= grid % g2;
+        hipLaunchKernelGGL(prefill_bf16_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a, geo);
+    }
     return hipGetLastError();
 }
 

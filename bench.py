@@ -49,6 +49,17 @@ TRAFFIC_FILES = {"prefill": "profiles/prefill_bf16_varlen16_pmc.md",
                  "decode": "profiles/decode_paged_b64_pmc.md"}
 
 
+PREFILL_WORKLOADS = {
+    "varlen": "varlen causal prefill: 16 sequences, lengths U[128,4096] (Lq = Lk), packed by "
+              "cu_seqlens, 32 Q / 8 KV heads, head_dim 128, bf16 in/out, new K/V stored to a "
+              "256-token paged cache first",
+    "long": "long causal prefill: 1 sequence of 32768 tokens, 32 Q / 8 KV heads, head_dim 128, "
+            "bf16 in/out, Q/K ~ N(0, 4), new K/V stored to a 256-token paged cache first",
+    "noncausal": "varlen non-causal prefill: the 16-sequence batch of the headline workload "
+                 "without the causal mask, bf16 in/out",
+}
+
+
 def source_sha(which: str) -> str:
     import hashlib
     h = hashlib.sha256()
@@ -291,10 +302,7 @@ def main():
         line.update({
             "value": round(pre["tflops_step"], 2), "unit": "TFLOP/s",
             "ms_per_step": round(pre["ms_step"], 4),
-            "config": {"workload": "varlen causal prefill: 16 sequences, lengths U[128,4096] "
-                                   "(Lq = Lk), packed by cu_seqlens, 32 Q / 8 KV heads, head_dim "
-                                   "128, bf16 in/out, new K/V stored to a 256-token paged cache "
-                                   "first",
+            "config": {"workload": PREFILL_WORKLOADS[args.prefill_workload],
                        "total_tokens": pre["total_tokens"], "algorithmic_flops": pre["flops"],
                        "step": "kv_store_slots + attn_prefill_varlen"},
             "roofline": {"bound": "mfma", "achieved": round(pre["tflops_kernel"], 2),

@@ -105,6 +105,29 @@ def test_bf16_empty_sequences():
     check_bf16(np32(run_varlen(vl)), oracle_varlen(vl), "bf16 empty seqs")
 
 
+def test_bf16_many_sequences():
+    """More sequences than the per-workgroup schedule tables hold (1100 >
+    1024), so the launch takes the strided unit schedule; lengths include 0."""
+    g = np.random.default_rng(11)
+    lens = g.integers(0, 41, size=1100)
+    lens[::97] = 0
+    vl = workloads.varlen(lens, lens, 4, 2, 128, torch.bfloat16, seed=12)
+    log("case bf16 1100 sequences (strided schedule)")
+    check_bf16(np32(run_varlen(vl)), oracle_varlen(vl), "bf16 1100 seqs")
+
+
+def test_bf16_loose_max_seqlen():
+    """max_seqlen_q / max_seqlen_k far above every actual length: the
+    schedule must skip the rows no sequence reaches."""
+    vl = workloads.varlen([130, 7, 64, 65], [130, 7, 64, 65], 8, 2, 128, torch.bfloat16, seed=13)
+    log("case bf16 loose max_seqlen")
+    out = attn.attn_prefill_varlen(dev(vl.q), dev(vl.k), dev(vl.v), dev(vl.cu_seqlens_q),
+                                   dev(vl.cu_seqlens_k), 5000, 5000, vl.softmax_scale, True,
+                                   out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_bf16(np32(out), oracle_varlen(vl), "bf16 loose max_seqlen")
+
+
 def test_bf16_one_hot_logits_exact():
     """Logit gap > 100 after scaling: the output equals V of the target key
     to bf16 precision of the inputs (weights are 1 and ~e^-100)."""
