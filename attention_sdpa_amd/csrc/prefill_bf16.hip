@@ -27,17 +27,22 @@
 //   operands come straight from the row-major V tile through the gfx950
 //   transposing LDS read (ds_read_b64_tr_b16); the accumulator again holds
 //   one query per lane, so any rescale is lane-local.
+// * Two groups of four wavefronts (one wave of each group per SIMD) run a
+//   ping-pong: while one group runs its matrix phase (the next tile's S^T and
+//   this tile's P V, MFMA after MFMA with LDS operand reads four steps
+//   ahead), the other computes a softmax on the vector ALUs; a workgroup
+//   barrier separates the half-steps.
 // * K/V tiles reach LDS by direct global->LDS loads (global_load_lds_dwordx4,
-//   no register staging) into a ring of three stages: the loads of tile t+2
-//   are issued while tile t is computed, and one barrier per tile suffices.
-//   16-byte chunks are XOR-swizzled (the swizzle is applied by choosing which
-//   global chunk each lane fetches) so that the operand reads are free of
-//   bank conflicts.
+//   no register staging) into rings of three stages.  The group entering its
+//   matrix phase issues them (one group all K tiles, the other all V tiles),
+//   so the softmax group issues no memory instructions.  16-byte chunks are
+//   XOR-swizzled (the swizzle is applied by choosing which global chunk each
+//   lane fetches) so that the operand reads are free of bank conflicts.
 // * Causal: tiles past the last visible key are never loaded; only tiles
 //   that cross the diagonal (or the sequence end) are masked.  Work units are
-//   issued heavy-first (latest query tiles first) and the KV head is the
-//   fastest-varying index, so that with 8 KV heads each XCD keeps reusing
-//   one head's K/V in its L2.
+//   dealt heavy-first (latest query blocks first) and the KV head is the
+//   fastest-varying index, so that each XCD keeps reusing few heads' K/V in
+//   its L2.
 // * Exponentials in base 2 with c = s*log2(e): p = 2^(fma(x, c, -r*c)) for a
 //   per-row reference r.  r follows the running maximum lazily: it is raised
 //   (and o', d' rescaled by 2^(r_old*c - r_new*c), the same rounded
@@ -412,30 +417,36 @@ prefill_bf16_kernel(VarlenArgs a, Geo geo) {
         return v;
     };
 
-    // ---- direct global -> LDS loads of one K or V tile ---------------------
-    // Wave w fills tile rows 8w .. 8w+7 with two 1 KiB loads; lane l lands at
-    // physical chunk (l & 15) of row 8w + 4i + (l >> 4) and fetches the
-    // logical chunk that the swizzle puts there.  Rows past the unit's last
-    // needed key repeat that key (finite data; those keys are masked).
-    const uint32_t k_lds0 = lds_addr(&sK[0][0]) + 8 * w * kD * 2;
-    const uint32_t v_lds0 = lds_addr(&sV[0][0]) + 8 * w * kD * 2;
-    const int r0 = 8 * w + dr, r1 = r0 + 4;            // this lane's tile rows
-    const uint32_t ck0 = (dc ^ swz_k(r0)) * 16, ck1 = (dc ^ swz_k(r1)) * 16;
-    const uint32_t cv0 = (dc ^ swz_v(r0)) * 16, cv1 = (dc ^ swz_v(r1)) * 16;
+    // ---- direct global -> LDS loads of the K and V tiles --------------------
+    // Group B loads every K tile and group A every V tile, each during its
+    // own matrix phase, so the group busy with the softmax issues no memory
+    // instructions.  Wave w' = w mod 4 of a group fills tile rows 16w' ..
+    // 16w'+15 with four 1 KiB loads; lane l lands at physical chunk (l & 15)
+    // of row 16w' + 4i + (l >> 4) and fetches the logical chunk that the
+    // tensor's swizzle puts there.  Rows past the unit's last needed key
+    // repeat that key (finite data; those keys are masked).
+    const int wq = w & 3;
+    const bf16 *my_src = grpA ? (const bf16 *)a.v : (const bf16 *)a.k;
+    const uint32_t my_lds0 = (grpA ? lds_addr(&sV[0][0]) : lds_addr(&sK[0][0])) + 16 * wq * kD * 2;
     const uint32_t row_bytes = (uint32_t)a.hkv * kD * 2;
-    // offsets of a full tile (no row clamped): no vector ALU work per load
-    const uint32_t fk0 = r0 * row_bytes + ck0, fk1 = r1 * row_bytes + ck1;
-    const uint32_t fv0 = r0 * row_bytes + cv0, fv1 = r1 * row_bytes + cv1;
+    const int rr0 = 16 * wq + dr;                          // this lane's rows: rr0 + 4i
+    uint32_t chk[4], full[4];                              // chunk offsets; full-tile offsets
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = rr0 + 4 * i;
+        chk[i] = (dc ^ (grpA ? swz_v(r) : swz_k(r))) * 16;
+        full[i] = r * row_bytes + chk[i];
+    }
 
     // ---- the K/V tile stream ----------------------------------------------
     // Stream position s runs over the tiles of this workgroup's units one
-    // after another; its ring stage is s mod 3.  Ring timing (half-steps of
-    // the ping-pong schedule below): K(s) is read in the two matrix
-    // half-steps before step s and refilled with K(s+3) at the barrier
-    // opening the odd half-step of step s; V(s) is read in the two matrix
-    // half-steps of step s and refilled with V(s+3) at the barrier opening
-    // step s+1 (the even half-step, which also waits for K(s+2) and V(s+1)).
-    // V(s) is always issued at the barrier after K(s), from the same rows.
+    // after another; its ring stage is s mod 3.  In the ping-pong schedule
+    // below, step s holds the matrix half-steps that read V(s) and K(s+1)
+    // (group A's after the even barrier E_s, group B's after the odd
+    // barrier O_s).  Group A loads V(s+2) in its matrix phase of step s and
+    // group B loads K(s+3) in its matrix phase of step s: the stages they
+    // overwrite were last read in step s-1.  Each group waits for its own
+    // loads at even barriers only: at E_s, A for V(s) and B for K(s+1).
     Unit C = find_unit(0, false);                          // compute cursor
     auto skip_empty = [&]() ATTN_INLINE {                  // units with rows but no key: zeros
         while (C.valid && C.n_tiles == 0) {
@@ -458,7 +469,7 @@ prefill_bf16_kernel(VarlenArgs a, Geo geo) {
         const int blk = ld_meta(a.block_table, idx);
         return (blk >= 0 && blk < a.num_blocks) ? blk : 0;   // bad id: stay in bounds
     };
-    KvCursor KU;
+    KvCursor KU;                                           // this wave's load cursor
     auto cursor_to = [&](const Unit &u) ATTN_INLINE {
         KU.k = u.k;
         KU.valid = u.valid;
@@ -490,68 +501,39 @@ prefill_bf16_kernel(VarlenArgs a, Geo geo) {
             }
         }
     };
-    int k_stage = 0, v_stage = 0;                          // stage of the next K / V load
-    int last_v = 0, last_k = 0;                            // loads issued at the last even/odd barrier
-    int vq_valid = 0, vq_tok = 0, vq_g = 0, vq_lim = 0;    // the V tile to load next
-    auto issue_k = [&]() ATTN_INLINE {
-        last_k = 0;
-        vq_valid = KU.valid;
+    int my_stage = 0;                                      // ring stage of this wave's next load
+    int last_n = 0;                                        // loads in this wave's latest batch
+    auto issue = [&]() ATTN_INLINE {
+        last_n = 0;
         if (KU.valid) {
             const int tok = paged ? KU.blk * a.block_size + KU.in_blk : KU.tok;
             const int lim = min(kBN - 1, KU.kv_end - 1 - KU.t * kBN);
-            const char *src = (const char *)a.k + ((int64_t)tok * a.hkv + KU.g) * (int64_t)(kD * 2);
-            const uint32_t lds = k_lds0 + k_stage * kStageBytes;
+            const bf16 *src = my_src + ((int64_t)tok * a.hkv + KU.g) * (int64_t)kD;
+            const uint32_t lds = my_lds0 + my_stage * kStageBytes;
             if (lim == kBN - 1) {
-                lds_dma16(src, fk0, lds);
-                lds_dma16(src, fk1, lds + 4 * kD * 2);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) lds_dma16(src, full[i], lds + 4 * i * kD * 2);
             } else {
-                lds_dma16(src, (uint32_t)min(r0, lim) * row_bytes + ck0, lds);
-                lds_dma16(src, (uint32_t)min(r1, lim) * row_bytes + ck1, lds + 4 * kD * 2);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    lds_dma16(src, (uint32_t)min(rr0 + 4 * i, lim) * row_bytes + chk[i], lds + 4 * i * kD * 2);
             }
-            vq_tok = tok;
-            vq_g = KU.g;
-            vq_lim = lim;
             advance();
-            last_k = 2;
+            last_n = 4;
         }
-        k_stage = (k_stage == 2) ? 0 : k_stage + 1;
-    };
-    auto issue_v = [&]() ATTN_INLINE {
-        last_v = 0;
-        if (vq_valid) {
-            const char *src = (const char *)a.v + ((int64_t)vq_tok * a.hkv + vq_g) * (int64_t)(kD * 2);
-            const uint32_t lds = v_lds0 + v_stage * kStageBytes;
-            if (vq_lim == kBN - 1) {
-                lds_dma16(src, fv0, lds);
-                lds_dma16(src, fv1, lds + 4 * kD * 2);
-            } else {
-                lds_dma16(src, (uint32_t)min(r0, vq_lim) * row_bytes + cv0, lds);
-                lds_dma16(src, (uint32_t)min(r1, vq_lim) * row_bytes + cv1, lds + 4 * kD * 2);
-            }
-            last_v = 2;
-        }
-        v_stage = (v_stage == 2) ? 0 : v_stage + 1;
+        my_stage = (my_stage == 2) ? 0 : my_stage + 1;
     };
     auto even_barrier = [&]() ATTN_INLINE {
-        const int pend = last_v + last_k;
-        if (pend == 4) stage_barrier<kWaitVm4>();
-        else if (pend == 2) stage_barrier<kWaitVm2>();
+        if (last_n == 4) stage_barrier<kWaitVm4>();
         else stage_barrier<kWaitVm0>();
-        issue_v();
     };
-    auto odd_barrier = [&]() ATTN_INLINE {
-        stage_barrier<kWaitNone>();
-        issue_k();
-    };
-    // stream prologue: K0 V0 K1 V1 K2
-    issue_k();
-    issue_v();
-    issue_k();
-    issue_v();
-    issue_k();
+    auto odd_barrier = [&]() ATTN_INLINE { stage_barrier<kWaitNone>(); };
+    // stream prologue: group A loads V0, V1; group B loads K0, K1, K2
+    issue();
+    issue();
+    if (!grpA) issue();
 
     int st = 0;                                            // ring stage of the unit's first tile
-    bool first = true;
     for (;;) {
         // ---- one unit: the ping-pong program on its tiles ----------------
         const WaveView V = wave_view(C);
@@ -706,10 +688,7 @@ prefill_bf16_kernel(VarlenArgs a, Geo geo) {
             else zero_p();
         } else {
             qk(st);
-            // half-step 0; for later units the V load of this position was
-            // issued at the end of the previous unit
-            if (first) even_barrier();
-            else stage_barrier<kWaitNone>();
+            stage_barrier<kWaitNone>();                    // half-step 0 (E_0 for group B)
             if (V.nw > 0) softmax(0);
             else zero_p();
         }
@@ -721,6 +700,7 @@ prefill_bf16_kernel(VarlenArgs a, Geo geo) {
             // every wave runs every step: past its last visible tile its P is
             // zero (adding exactly 0), and the last step's S^T is unused
             mma(st1, st);
+            issue();
             __builtin_amdgcn_s_setprio(0);
             if (grpA) odd_barrier();
             else even_barrier();
@@ -759,7 +739,6 @@ prefill_bf16_kernel(VarlenArgs a, Geo geo) {
         C = find_unit(C.k + 1, false);
         skip_empty();
         if (!C.valid) break;
-        first = false;
     }
     // no direct-to-LDS load may outlive the workgroup's LDS allocation
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
