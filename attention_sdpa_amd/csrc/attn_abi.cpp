@@ -28,14 +28,14 @@ int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; 
 // Split size of the decode key range: the caller's (a positive multiple of
 // 64), or, for 0, one that gives the launch a few thousand workgroups.
 int resolve_split(int batch, int num_kv_heads, int max_blocks_per_seq, int block_size, int split) {
+    (void)batch;
+    (void)num_kv_heads;
     if (split < 0 || split % 64 != 0) return -1;
     if (split > 0) return split;
+    // the persistent split kernel balances whole splits across workgroups:
+    // 256 keys (one 64-key chunk per wavefront) keeps that balance fine
     const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
-    const int64_t units = (int64_t)batch * num_kv_heads;
-    const int64_t want_splits = (4096 + units - 1) / units;
-    int64_t s = (cap + want_splits - 1) / want_splits;
-    s = ((s + 255) / 256) * 256;
-    if (s < 256) s = 256;
+    int64_t s = 256;
     if (s > cap) s = ((cap + 63) / 64) * 64;
     return (int)s;
 }
@@ -60,7 +60,7 @@ bool decode_layout(int batch, int hq, int hkv, int d, int mbs, int bs, int split
     L->max_splits = (int)ns;
     L->o_bytes = rows * (size_t)d * sizeof(float);
     L->ml_off = (L->o_bytes + 255) / 256 * 256;
-    L->total = L->ml_off + rows * 2 * sizeof(float);
+    L->total = L->ml_off + rows * 4 * sizeof(float);   // m, d', split count, pad
     return true;
 }
 

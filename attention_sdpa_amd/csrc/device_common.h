@@ -41,6 +41,31 @@ __device__ __forceinline__ int32_t ld_meta(const int32_t *p, int64_t i) {
     return ((const __attribute__((address_space(4))) int32_t *)(p))[i];
 }
 
+// Direct global->LDS load of 16 bytes per lane (global_load_lds_dwordx4 with
+// a scalar base address and a per-lane 32-bit offset): lane l's 16 bytes at
+// sbase + voff land at LDS byte address lds + 16*l.  Issued from inline
+// assembly so that the compiler, which cannot tell which LDS buffer a later
+// LDS read touches, does not wait for every such load before every read;
+// the kernels order them themselves (s_waitcnt vmcnt, plus s_barrier where
+// several waves share a buffer).  M0 carries the LDS address and is
+// restored afterwards.
+__device__ __forceinline__ void lds_dma16(const void *sbase, uint32_t voff, uint32_t lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(sbase), "s"(lds)
+        : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const ATTN_LDS void *)p;
+}
+
 // 16-byte global load/store helpers.
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 __device__ __forceinline__ void st16(void *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }

@@ -58,7 +58,7 @@ struct DecodeArgs {
     int split_tokens;  // resolved, > 0, multiple of 64
     int max_splits;    // ceil(max_blocks_per_seq * block_size / split_tokens)
     float *ws_o;       // [batch, hq, max_splits, d]
-    float *ws_ml;      // [batch, hq, max_splits, 2]
+    float *ws_ml;      // [batch, hq, max_splits, 4]: m, d', split count (int bits), pad
     int out_f32;
 };
 

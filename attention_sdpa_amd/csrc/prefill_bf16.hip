@@ -89,30 +89,6 @@ constexpr int kSchedValu = 0x0002;
 constexpr int kSchedMfma = 0x0008;
 constexpr int kSchedDsRead = 0x0100;
 
-// Direct global->LDS load of 16 bytes per lane (global_load_lds_dwordx4 with
-// a scalar base address and a per-lane 32-bit offset): lane l's 16 bytes at
-// sbase + voff land at LDS byte address lds + 16*l.  Issued from inline
-// assembly so that the compiler, which cannot tell which ring stage a later
-// LDS read touches, does not wait for every such load before every read;
-// the kernel orders them itself (s_waitcnt vmcnt + s_barrier).  M0 carries
-// the LDS address and is restored afterwards.
-__device__ __forceinline__ void lds_dma16(const void *sbase, uint32_t voff, uint32_t lds) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %3\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, %2\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(voff), "s"(sbase), "s"(lds)
-        : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-    return (uint32_t)(uintptr_t)(const ATTN_LDS void *)p;
-}
-
 // All waves' loads of the current stage have landed; nobody still reads the
 // stage about to be refilled.  The empty asm statements keep the compiler
 // from moving memory operations across the barrier.

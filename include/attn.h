@@ -134,8 +134,9 @@ int attn_prefill_varlen(const void *q, const void *k, const void *v, void *o,
 
 /*
  * attn_decode_workspace_bytes -- bytes of device workspace attn_decode_paged
- * needs for these sizes (0 if the sizes are invalid).  split_tokens as in
- * attn_decode_paged.
+ * needs for these sizes (0 if the sizes are invalid): one fp32 partial row
+ * of head_dim values plus 4 fp32 words (m, d', run length, pad) per
+ * (sequence, query head, split).  split_tokens as in attn_decode_paged.
  */
 size_t attn_decode_workspace_bytes(int batch, int num_q_heads, int num_kv_heads,
                                    int head_dim, int max_blocks_per_seq,
@@ -154,10 +155,13 @@ size_t attn_decode_workspace_bytes(int batch, int num_q_heads, int num_kv_heads,
  * clipped to max_blocks_per_seq * block_size.
  *
  * The key range of each (sequence, KV head) is cut into splits of
- * split_tokens keys (0 = the library's choice, else a positive multiple of
- * 64); each split's partial state (m, d', unnormalised o') goes to the
- * workspace and a second kernel merges the partials with the same
- * rescaling the online recurrence uses.
+ * split_tokens keys (0 = the library's choice, 256; else a positive
+ * multiple of 64), which are dealt in equal contiguous runs to persistent
+ * workgroups.  A workgroup keeps the online state (m, d', unnormalised o')
+ * across the consecutive splits of one sequence it reads and stores one
+ * partial per run; a second kernel merges the partials with the same
+ * rescaling the online recurrence uses.  The result does not depend on
+ * how the runs fall, up to floating-point rounding order.
  *
  *   q             [batch, num_q_heads, head_dim], in_dtype
  *   k_cache,

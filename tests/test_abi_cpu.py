@@ -135,7 +135,12 @@ def test_decode_validation(lib):
     assert decode(lib, ws=None) == E.ATTN_ERR_WORKSPACE
     assert decode(lib, wsb=need - 1) == E.ATTN_ERR_WORKSPACE
     assert decode(lib, ws=MIS) == E.ATTN_ERR_WORKSPACE   # must be 256-byte aligned
-    # split size changes the workspace exactly as the partial layout says
-    w512 = lib.attn_decode_workspace_bytes(4, 32, 8, 128, 32, 256, 512)
-    w1024 = lib.attn_decode_workspace_bytes(4, 32, 8, 128, 32, 256, 1024)
-    assert w512 >= 4 * 32 * 16 * 130 * 4 and w1024 >= 4 * 32 * 8 * 130 * 4 and w512 > w1024
+    # the workspace is exactly the documented partial layout: per (sequence,
+    # query head, split) d fp32 values, then (256-aligned) 4 fp32 words
+    def layout(batch, hq, d, mbs, bs, split):
+        rows = batch * hq * (-(-mbs * bs // split))
+        return (rows * d * 4 + 255) // 256 * 256 + rows * 16
+    for split in (64, 512, 1024):
+        assert lib.attn_decode_workspace_bytes(4, 32, 8, 128, 32, 256, split) == layout(4, 32, 128, 32, 256, split)
+    assert need == layout(4, 32, 128, 32, 256, 256)          # the default split is 256 keys
+    assert lib.attn_decode_workspace_bytes(2, 8, 8, 128, 1, 128, 0) == layout(2, 8, 128, 1, 128, 128)
