@@ -38,6 +38,14 @@
 //   so the softmax group issues no memory instructions.  16-byte chunks are
 //   XOR-swizzled (the swizzle is applied by choosing which global chunk each
 //   lane fetches) so that the operand reads are free of bank conflicts.
+// * Unit boundaries: the last step of a unit forms P V only (no S^T is
+//   needed), and each group loads the next unit's Q rows right after it; the
+//   group then writes its O in the half-step its softmax would have taken,
+//   while the other group is in its matrix phase, and forms the next unit's
+//   first S^T one half-step later.  The O stores are buffer stores against a
+//   resource spanning the unit's valid rows (rows past the sequence end are
+//   dropped), 8 per wave after one exchange of the lane halves, so the wait
+//   counts that follow are exact.
 // * Causal: tiles past the last visible key are never loaded; only tiles
 //   that cross the diagonal (or the sequence end) are masked.  Work units are
 //   dealt heavy-first (latest query blocks first) and the KV head is the
@@ -50,6 +58,8 @@
 //   p <= 256 and leaves the result unchanged in exact arithmetic.
 // * Row sums are accumulated from the bf16-rounded P with v_dot2_f32_bf16,
 //   i.e. from exactly the weights the P V product uses.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -82,7 +92,15 @@ constexpr int kWaitVm2 = 0x0072;
 constexpr int kWaitVm4 = 0x0074;
 constexpr int kWaitVm6 = 0x0076;
 constexpr int kWaitVm8 = 0x0078;
-constexpr int kWaitNone = 0xC07F;   // no counter wait (vmcnt 63, lgkmcnt 15)
+constexpr int kWaitVm12 = 0x007C;
+constexpr int kWaitVm16 = 0x4070;   // vmcnt bits 5:4 live in bits 15:14
+constexpr int kWaitVm20 = 0x4074;
+constexpr int kWaitNone = 0xC07F;   // vmcnt 63: no memory wait (LDS and scalar: lgkmcnt 0)
+
+// Buffer resource word 3 for raw (unformatted, unswizzled) buffer access.
+constexpr int kBufferFlags = 0x00020000;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // instruction classes for __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedValu = 0x0002;
@@ -424,7 +442,7 @@ prefill_bf16_kernel(VarlenArgs a, Geo geo) {
     // overwrite were last read in step s-1.  Each group waits for its own
     // loads at even barriers only: at E_s, A for V(s) and B for K(s+1).
     Unit C = find_unit(0, false);                          // compute cursor
-    auto skip_empty = [&]() ATTN_INLINE {                  // units with rows but no key: zeros
+    auto skip_empty = [&](Unit &C) ATTN_INLINE {           // units with rows but no key: zeros
         while (C.valid && C.n_tiles == 0) {
             const WaveView v = wave_view(C);
             if (v.row_valid) {
@@ -438,7 +456,7 @@ prefill_bf16_kernel(VarlenArgs a, Geo geo) {
             C = find_unit(C.k + 1, false);
         }
     };
-    skip_empty();
+    skip_empty(C);
     if (!C.valid) return;
 
     auto load_blk = [&](int idx) ATTN_INLINE {
@@ -477,6 +495,10 @@ prefill_bf16_kernel(VarlenArgs a, Geo geo) {
             }
         }
     };
+    // Vector-memory operations this wave may leave outstanding at its next
+    // waiting barrier: its latest K/V batch, plus any O stores issued after
+    // it (the counter retires in issue order).
+    int vm_allow = 0;
     int my_stage = 0;                                      // ring stage of this wave's next load
     int last_n = 0;                                        // loads in this wave's latest batch
     auto issue = [&]() ATTN_INLINE {
@@ -497,12 +519,22 @@ prefill_bf16_kernel(VarlenArgs a, Geo geo) {
             advance();
             last_n = 4;
         }
+        vm_allow = last_n;
         my_stage = (my_stage == 2) ? 0 : my_stage + 1;
     };
-    auto even_barrier = [&]() ATTN_INLINE {
-        if (last_n == 4) stage_barrier<kWaitVm4>();
-        else stage_barrier<kWaitVm0>();
+    // The wait of this wave's next waiting barrier: the vector-memory
+    // operations (vm_allow, below) it may leave outstanding.
+    auto wait_barrier = [&]() ATTN_INLINE {
+        switch (vm_allow) {
+            case 4: stage_barrier<kWaitVm4>(); break;
+            case 8: stage_barrier<kWaitVm8>(); break;
+            case 12: stage_barrier<kWaitVm12>(); break;
+            case 16: stage_barrier<kWaitVm16>(); break;
+            case 20: stage_barrier<kWaitVm20>(); break;
+            default: stage_barrier<kWaitVm0>(); break;
+        }
     };
+    auto even_barrier = [&]() ATTN_INLINE { wait_barrier(); };
     auto odd_barrier = [&]() ATTN_INLINE { stage_barrier<kWaitNone>(); };
     // stream prologue: group A loads V0, V1; group B loads K0, K1, K2
     issue();
@@ -510,25 +542,81 @@ prefill_bf16_kernel(VarlenArgs a, Geo geo) {
     if (!grpA) issue();
 
     int st = 0;                                            // ring stage of the unit's first tile
+    bf16x8 qf[KK];
+    f32x16 o[DB];
+    float m_ref, mc_ref, l_run;
+    f32x16 sacc[2];
+    bf16x8 pb[4];
+    // Q rows of unit u into qf.  A row past the sequence end reads the
+    // sequence's first row instead: finite values confined to its own lane
+    // pair, whose output is dropped.
+    auto load_q = [&](const Unit &u) ATTN_INLINE {
+        const WaveView qv = wave_view(u);
+        const bf16 *qp = (const bf16 *)a.q + (((int64_t)u.q0 + (qv.row_valid ? qv.pos : 0)) * a.hq + qv.head) * (int64_t)kD + 8 * hf;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            uint4 tq = ld16(qp + 16 * kk);
+            qf[kk] = *reinterpret_cast<bf16x8 *>(&tq);
+        }
+    };
+    // O = o' / d' of unit u.  Buffer stores against a resource that spans
+    // the unit's valid rows: stores of rows past the sequence end fall
+    // outside it and are dropped, so every wave issues exactly 8 (bf16) or
+    // 16 (fp32) stores.
+    auto store_o = [&](const Unit &u, const WaveView &v) ATTN_INLINE {
+        float l_tot;
+        {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+            l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        }
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        const int esz = a.out_f32 ? 4 : 2;
+        const int rows = min(geo.pos_per_wg, u.Lq - u.p0);
+        char *ob = (char *)a.o + ((int64_t)(u.q0 + u.p0) * a.hq) * (int64_t)(kD * esz);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(ob, (short)0, rows * a.hq * kD * esz, kBufferFlags);
+        const int voff = ((v.pos - u.p0) * a.hq + v.head) * kD * esz;
+        if (a.out_f32) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const int d0 = 32 * db + 8 * a4 + 4 * hf;
+                    const u32x4 r = {__float_as_uint(o[db][4 * a4] * inv), __float_as_uint(o[db][4 * a4 + 1] * inv),
+                                     __float_as_uint(o[db][4 * a4 + 2] * inv), __float_as_uint(o[db][4 * a4 + 3] * inv)};
+                    __builtin_amdgcn_raw_buffer_store_b128(r, rs, voff + 4 * d0, 0, 0);
+                }
+        } else {
+            // lane n holds d = 8m + 0..3 of its row and lane n + 32 holds
+            // d = 8m + 4..7; one exchange of the two halves gives each lane 8
+            // consecutive d values, so a store covers 32 bytes of each row
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int pr = 0; pr < 2; ++pr) {
+                    bf16x4 y, x;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        y[e] = f32_to_bf16(o[db][8 * pr + e] * inv);
+                        x[e] = f32_to_bf16(o[db][8 * pr + 4 + e] * inv);
+                    }
+                    const u32x2 yu = *reinterpret_cast<u32x2 *>(&y), xu = *reinterpret_cast<u32x2 *>(&x);
+                    const auto s0 = __builtin_amdgcn_permlane32_swap(yu[0], xu[0], false, false);
+                    const auto s1 = __builtin_amdgcn_permlane32_swap(yu[1], xu[1], false, false);
+                    const u32x4 r = {s0[0], s1[0], s0[1], s1[1]};
+                    __builtin_amdgcn_raw_buffer_store_b128(r, rs, voff + 2 * (32 * db + 16 * pr + 8 * hf), 0, 0);
+                }
+        }
+    };
+    load_q(C);
+    bool first = true;
+    Unit Cn;
     for (;;) {
         // ---- one unit: the ping-pong program on its tiles ----------------
         const WaveView V = wave_view(C);
         const int ntl = C.n_tiles;
-        bf16x8 qf[KK];
-        {
-            const bf16 *qp = (const bf16 *)a.q + (((int64_t)C.q0 + (V.row_valid ? V.pos : 0)) * a.hq + V.head) * (int64_t)kD + 8 * hf;
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                uint4 tq = V.row_valid ? ld16(qp + 16 * kk) : make_uint4(0, 0, 0, 0);
-                qf[kk] = *reinterpret_cast<bf16x8 *>(&tq);
-            }
-        }
-        f32x16 o[DB];
 #pragma unroll
         for (int i = 0; i < DB; ++i) o[i] = f32x16{};
-        float m_ref = kNegInf, mc_ref = 0.f, l_run = 0.f;
-        f32x16 sacc[2];
-        bf16x8 pb[4];
+        m_ref = kNegInf; mc_ref = 0.f; l_run = 0.f;
         const bf16x2 ones2 = {(bf16)1.f, (bf16)1.f};
         const int k_row = perm23(n);
         const int gq = lane >> 4, s16 = lane & 15;
@@ -562,7 +650,8 @@ prefill_bf16_kernel(VarlenArgs a, Geo geo) {
         // O^T += V^T P^T for the tile in V stage vs, with the row sums from
         // the same bf16 weights.  The two products alternate MFMA by MFMA;
         // the operands of step i + kAhead are read from LDS during step i.
-        auto mma = [&](int ks, int vs) ATTN_INLINE {
+        auto mma = [&](int ks, int vs, auto with_qk) ATTN_INLINE {
+            constexpr bool kQK = decltype(with_qk)::value;
             constexpr int kAhead = 4;
             const bf16 *Kt = &sK[0][0] + ks * kTileElems;
             const bf16 *Vt = &sV[0][0] + vs * kTileElems;
@@ -586,16 +675,20 @@ prefill_bf16_kernel(VarlenArgs a, Geo geo) {
             };
 #pragma unroll
             for (int i = 0; i < kAhead; ++i) {
-                read_k(i);
+                if constexpr (kQK) read_k(i);
                 read_v(i);
             }
-            sacc[0] = f32x16{};
-            sacc[1] = f32x16{};
+            if constexpr (kQK) {
+                sacc[0] = f32x16{};
+                sacc[1] = f32x16{};
+            }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                sacc[i >> 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kbuf[i], qf[i & 7], sacc[i >> 3], 0, 0, 0);
-                if (i + kAhead < 16) read_k(i + kAhead);
+                if constexpr (kQK) {
+                    sacc[i >> 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kbuf[i], qf[i & 7], sacc[i >> 3], 0, 0, 0);
+                    if (i + kAhead < 16) read_k(i + kAhead);
+                }
                 const int jj = i >> 2, db = i & 3;
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vbuf[i], pb[jj], o[db], 0, 0, 0);
                 if (i + kAhead < 16) read_v(i + kAhead);
@@ -654,28 +747,35 @@ prefill_bf16_kernel(VarlenArgs a, Geo geo) {
             for (int jj = 0; jj < 4; ++jj) pb[jj] = bf16x8{};
         };
 
-        // prologue: K(s0) (and this unit's Q rows) landed.  Waiting for
-        // everything also retires the previous unit's O stores.
-        stage_barrier<kWaitVm0>();                         // half-step -2
-        if (grpA) qk(st);
-        stage_barrier<kWaitNone>();                        // half-step -1
-        if (grpA) {
-            if (V.nw > 0) softmax(0);
-            else zero_p();
+        // ---- prologue: S^T and P of the unit's first tile ------------------
+        // The first time, K(s0) and the Q rows are waited for outright.
+        // Later units follow their predecessor's last steps directly: each
+        // group forms its first S^T in the half-step after its own O stores
+        // (the two groups one half-step apart, as in the step loop).
+        if (first) {
+            stage_barrier<kWaitVm0>();
+            if (grpA) qk(st);
+            stage_barrier<kWaitNone>();
+            if (!grpA) {
+                qk(st);
+                stage_barrier<kWaitNone>();
+            }
         } else {
+            wait_barrier();                                // this wave's Q rows landed
             qk(st);
-            stage_barrier<kWaitNone>();                    // half-step 0 (E_0 for group B)
-            if (V.nw > 0) softmax(0);
-            else zero_p();
+            stage_barrier<kWaitNone>();
         }
-        for (int t = 0; t < ntl; ++t) {
+        if (V.nw > 0) softmax(0);
+        else zero_p();
+        // ---- all steps but the last ----------------------------------------
+        for (int t = 0; t + 1 < ntl; ++t) {
             const int st1 = (st == 2) ? 0 : st + 1;
             if (grpA) even_barrier();
             else odd_barrier();
             __builtin_amdgcn_s_setprio(1);
             // every wave runs every step: past its last visible tile its P is
-            // zero (adding exactly 0), and the last step's S^T is unused
-            mma(st1, st);
+            // zero (adding exactly 0)
+            mma(st1, st, std::true_type{});
             issue();
             __builtin_amdgcn_s_setprio(0);
             if (grpA) odd_barrier();
@@ -684,38 +784,30 @@ prefill_bf16_kernel(VarlenArgs a, Geo geo) {
             else zero_p();
             st = st1;
         }
-        if (grpA) stage_barrier<kWaitNone>();              // B's last half-step
-
-        // ---- O = o' / d' for this wave's valid rows ----
-        if (V.row_valid) {
-            float l_tot;
-            {
-                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
-                l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-            }
-            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-            const int64_t obase = (((int64_t)C.q0 + V.pos) * a.hq + V.head) * (int64_t)kD;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int a4 = 0; a4 < 4; ++a4) {
-                    const int d0 = 32 * db + 8 * a4 + 4 * hf;
-                    const float v0 = o[db][4 * a4] * inv, v1 = o[db][4 * a4 + 1] * inv;
-                    const float v2 = o[db][4 * a4 + 2] * inv, v3 = o[db][4 * a4 + 3] * inv;
-                    if (a.out_f32) {
-                        *reinterpret_cast<float4 *>((float *)a.o + obase + d0) = make_float4(v0, v1, v2, v3);
-                    } else {
-                        bf16x4 r;
-                        r[0] = f32_to_bf16(v0); r[1] = f32_to_bf16(v1);
-                        r[2] = f32_to_bf16(v2); r[3] = f32_to_bf16(v3);
-                        *reinterpret_cast<bf16x4 *>((bf16 *)a.o + obase + d0) = r;
-                    }
-                }
+        // ---- the last step: P V only, then the next unit's Q rows ----------
+        {
+            const int st1 = (st == 2) ? 0 : st + 1;
+            if (grpA) even_barrier();
+            else odd_barrier();
+            __builtin_amdgcn_s_setprio(1);
+            mma(st1, st, std::false_type{});
+            __builtin_amdgcn_s_setprio(0);
+            Cn = find_unit(C.k + 1, false);
+            skip_empty(Cn);
+            if (Cn.valid) load_q(Cn);                      // before the batch: the next wait covers it
+            issue();
+            if (grpA) odd_barrier();
+            else even_barrier();
+            st = st1;
         }
-        C = find_unit(C.k + 1, false);
-        skip_empty();
+        // ---- O of this unit, in the half-step its softmax would take --------
+        store_o(C, V);
+        vm_allow = last_n + (a.out_f32 ? 16 : 8);
+        C = Cn;
         if (!C.valid) break;
+        first = false;
     }
+    if (grpA) stage_barrier<kWaitNone>();                  // B's last half-step
     // no direct-to-LDS load may outlive the workgroup's LDS allocation
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
 }
