@@ -15,10 +15,10 @@
 // Decode reads every K/V byte once and does ~4 flops per byte, so it is
 // HBM-bound: the design keeps as many bytes in flight as possible.
 // * The split kernel is persistent, two 4-wavefront workgroups per CU; each
-//   wavefront has a whole 64-key chunk (32 KiB of K and V) in flight at a
-//   time.  (Measured: a plain streaming read peaks with 32 KiB per
-//   wavefront at 8 wavefronts per CU; 32-key chunks at 16 wavefronts per CU
-//   were slightly slower here.)
+//   wavefront has a whole 32-key chunk (16 KiB of K and V) in flight at a
+//   time.  (Measured on this cache layout: a streaming read of 32-key chunks
+//   by direct-to-LDS loads at 8 wavefronts per CU runs as fast as 64-key
+//   chunks at 4 or 8 wavefronts per CU, ~5.8 TB/s.)
 // * Work items are (sequence b, KV head g, split s), s < ceil(L_b / S).
 //   Workgroup i of G serves head g = i mod hkv and takes the contiguous
 //   range [r*J/R, (r+1)*J/R) of that head's J items (b, s), r = i / hkv,
@@ -27,11 +27,13 @@
 //   per run of splits (a segment), stored at the run's first split together
 //   with the run length, which the combine pass uses to step from one
 //   stored partial to the next.
-// * Inside an item the 4 wavefronts take 64-key chunks round-robin.  K rows
-//   go from global memory straight into registers as the A operand of
-//   S^T = K Q^T (v_mfma_f32_16x16x32_bf16, keys = M, query heads = N); V
-//   rows go by direct global->LDS loads into a per-wavefront buffer and come
-//   back transposed (ds_read_b64_tr_b16) as the A operand of O^T += V^T P^T.
+// * Inside an item the 4 wavefronts take 32-key chunks round-robin.  K and V
+//   rows go by direct global->LDS loads (four whole 256-byte rows per
+//   instruction) into per-wavefront buffers.  K comes back by 16-byte reads
+//   as the A operand of S^T = K Q^T (v_mfma_f32_16x16x32_bf16, keys = M,
+//   query heads = N); V comes back transposed (ds_read_b64_tr_b16) as the A
+//   operand of O^T += V^T P^T.  (Reading K straight into registers in the
+//   operand layout touches 16 rows per instruction and streams ~6 % slower.)
 // * Block ids are read one item ahead, so no chunk waits on the block
 //   table before its K/V loads.
 #include "device_common.h"
@@ -43,13 +45,15 @@ namespace {
 
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = kDecWaves * 64;
-constexpr int kChunk = 64;        // keys per wavefront step (32 KiB of K and V)
+constexpr int kChunk = 32;        // keys per wavefront step (16 KiB of K and V)
 constexpr int kDecWgsPerCu = 2;   // persistent workgroups per CU (8 wavefronts)
 constexpr int kWaitAll = 0x0070;   // s_waitcnt vmcnt(0) lgkmcnt(0)
 
 // 16-byte-chunk swizzle of a V row in the LDS buffer (conflict-free
 // transposing reads)
 __device__ __forceinline__ int swz_dv(int row) { return (row & 7) << 1; }
+// ... and of a K row (conflict-free 16-byte reads of 16 consecutive rows)
+__device__ __forceinline__ int swz_dk(int row) { return row & 15; }
 
 template <int D>
 __global__ void __launch_bounds__(kDecThreads, kDecWgsPerCu)
@@ -60,6 +64,7 @@ decode_split_kernel(DecodeArgs a) {
     constexpr int VI = kChunk / 4;      // direct-to-LDS loads per V chunk (4 rows each)
     constexpr int JJ = kChunk / 32;     // 32-key MFMA steps of P V
     static_assert(kChunk % 32 == 0, "chunks are whole 32-key MFMA steps");
+    __shared__ __align__(16) bf16 sK[kDecWaves][kChunk * D];
     __shared__ __align__(16) bf16 sV[kDecWaves][kChunk * D];
     __shared__ float sMerge[kDecWaves][16][2];
     __shared__ int sStart[4];
@@ -155,6 +160,8 @@ decode_split_kernel(DecodeArgs a) {
     const float cl = a.scale_log2;
     bf16 *vbuf = sV[w];
     const uint32_t vbuf_lds = lds_addr(vbuf);
+    bf16 *kbuf = sK[w];
+    const uint32_t kbuf_lds = lds_addr(kbuf);
     const int64_t rstride = (int64_t)a.hkv * D;        // elements between key rows
     const uint32_t row_bytes = (uint32_t)rstride * 2;
 
@@ -163,34 +170,44 @@ decode_split_kernel(DecodeArgs a) {
         const bool bok = blk >= 0 && blk < a.num_blocks;
         const int64_t base = ((((int64_t)(bok ? blk : 0) * a.block_size + c0 % a.block_size) * a.hkv + g) * D);
         const int last = kend - 1 - c0;                    // last valid row of the chunk
-        // V -> LDS: load i covers rows 4i .. 4i+3; lane l lands at physical
-        // chunk (l & 15) of row 4i + (l >> 4) and fetches the logical chunk
-        // the swizzle puts there.  Rows past the split end repeat its last
-        // key (finite data; their weights are zero).
+        // K and V -> LDS: load i covers rows 4i .. 4i+3 (four whole 256-byte
+        // rows per instruction); lane l lands at physical chunk (l & 15) of
+        // row 4i + (l >> 4) and fetches the logical chunk the swizzle puts
+        // there.  Rows past the split end repeat its last key (finite data;
+        // their weights are zero).
         if (bok) {
+            const bf16 *ksrc = (const bf16 *)a.k_cache + base;
             const bf16 *vsrc = (const bf16 *)a.v_cache + base;
 #pragma unroll
             for (int i = 0; i < VI; ++i) {
                 const int row = 4 * i + gq;
-                const uint32_t off = (uint32_t)min(row, last) * row_bytes + (uint32_t)((n ^ swz_dv(row)) * 16);
-                lds_dma16(vsrc, off, vbuf_lds + i * 4 * D * 2);
+                const uint32_t roff = (uint32_t)min(row, last) * row_bytes;
+                lds_dma16(ksrc, roff + (uint32_t)((n ^ swz_dk(row)) * 16), kbuf_lds + i * 4 * D * 2);
+                lds_dma16(vsrc, roff + (uint32_t)((n ^ swz_dv(row)) * 16), vbuf_lds + i * 4 * D * 2);
             }
         } else {
             // a block id outside the pool reads as zero rows
 #pragma unroll
-            for (int i = 0; i < VI; ++i) st16(vbuf + (4 * i + gq) * D + 8 * n, make_uint4(0, 0, 0, 0));
+            for (int i = 0; i < VI; ++i) {
+                st16(kbuf + (4 * i + gq) * D + 8 * n, make_uint4(0, 0, 0, 0));
+                st16(vbuf + (4 * i + gq) * D + 8 * n, make_uint4(0, 0, 0, 0));
+            }
         }
-        // K: row blocks of 16 keys; lane holds key (16mb + n) and, for k-step
-        // kk, d in [32kk + 8gq, +8) (Q uses the same order of d), so that one
-        // load instruction reads 64 contiguous bytes of each of 16 key rows
+        // the K and V rows (direct loads, or the zero fill) must have landed
+        __builtin_amdgcn_s_waitcnt(kWaitAll);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // K operands: row blocks of 16 keys; lane holds key (16mb + n) and,
+        // for k-step kk, d in [32kk + 8gq, +8) (Q uses the same order of d)
         uint4 kr[MB][KK];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            const bool ok = bok && 16 * mb + n <= last;
-            const bf16 *kp = (const bf16 *)a.k_cache + base + (int64_t)(16 * mb + n) * rstride + 8 * gq;
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) kr[mb][kk] = ok ? ld16(kp + 32 * kk) : make_uint4(0, 0, 0, 0);
-        }
+            for (int kk = 0; kk < KK; ++kk) {
+                const int row = 16 * mb + n;
+                kr[mb][kk] = *reinterpret_cast<const uint4 *>(kbuf + row * D + (((4 * kk + gq) ^ swz_dk(row)) * 8));
+            }
         // S^T = K Q^T
         f32x4 sacc[MB];
 #pragma unroll
@@ -234,11 +251,6 @@ decode_split_kernel(DecodeArgs a) {
         mc_run = mc_new;
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[db] *= alpha;
-        // the V rows (direct loads, or the zero fill) must have landed
-        __builtin_amdgcn_s_waitcnt(kWaitAll);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         // O^T += V^T P^T, 32 keys per step (keys 32jj + 4gq + e and +16)
 #pragma unroll
         for (int jj = 0; jj < JJ; ++jj)
@@ -254,7 +266,7 @@ decode_split_kernel(DecodeArgs a) {
                 const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
                 o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[jj], o[db], 0, 0, 0);
             }
-        // the reads of vbuf must finish before the next chunk's loads land
+        // the reads of kbuf and vbuf must finish before the next chunk's loads land
         __builtin_amdgcn_s_waitcnt(kWaitAll);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
