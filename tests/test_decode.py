@@ -108,3 +108,16 @@ def test_full_paged_decode_64():
     check_bf16(np32(got), ref, "decode 64 (all rows)")
     for split in (256, 2048):
         check_bf16(np32(run_decode(dc, split)), ref, f"decode 64 split {split}")
+
+
+def test_decode_shared_prefix_blocks():
+    """Decode over block tables whose first blocks are shared by every
+    sequence (one cached prompt stored once): the new token of each sequence
+    attends to the prompt, its own cached tokens and itself."""
+    pp = workloads.shared_prefix_prefill(n_seqs=8, shared_blocks=4, own_lo=0, own_hi=700,
+                                         q_lo=1, q_hi=1, hq=32, hkv=8, block_size=256, seed=41)
+    dc = workloads.Decode(pp.q.view(8, 32, 128), pp.softmax_scale, pp.paged, pp.name)
+    assert (dc.paged.block_table[:, :4] == dc.paged.block_table[0, :4]).all()
+    log("case decode shared prefix blocks")
+    for split in (0, 256):
+        check_bf16(np32(run_decode(dc, split)), oracle_decode(dc), f"decode shared prefix split {split}")

@@ -175,6 +175,18 @@ def test_bf16_prefix_prefill_paged(block_size):
     check_bf16(np32(run_prefix(pp)), oracle_prefix(pp), f"prefix bs{block_size}")
 
 
+def test_bf16_shared_prefix_blocks():
+    """Block tables that share their first physical blocks (one cached prompt
+    read by every sequence; the page-table picture of the Prefill section has
+    two sequences pointing at the same block) give the oracle's result for the
+    logical per-sequence K/V."""
+    pp = workloads.shared_prefix_prefill(n_seqs=6, shared_blocks=3, own_lo=0, own_hi=300,
+                                         q_lo=1, q_hi=150, hq=8, hkv=2, block_size=64, seed=31)
+    assert (pp.paged.block_table[:, :3] == pp.paged.block_table[0, :3]).all()
+    log("case bf16 shared prefix blocks")
+    check_bf16(np32(run_prefix(pp)), oracle_prefix(pp), "shared prefix")
+
+
 def test_paged_block_permutation_bit_identical():
     """The same logical K/V laid out in two differently permuted pools gives
     bit-identical outputs (arithmetic order depends on logical positions only),

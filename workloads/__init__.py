@@ -257,6 +257,61 @@ def prefix_prefill(n_seqs=32, q_lo=1, q_hi=512, p_lo=1024, p_hi=16384, hq=32, hk
                          f"prefix_prefill_{n_seqs}x(q[{q_lo},{q_hi}]+p[{p_lo},{p_hi}])_bs{block_size}")
 
 
+def shared_prefix_prefill(n_seqs=6, shared_blocks=3, own_lo=0, own_hi=300, q_lo=1, q_hi=150,
+                          hq=8, hkv=2, d=128, block_size=64, seed=0,
+                          dtype=torch.bfloat16) -> PrefixPrefill:
+    """Sequences that share a cached prompt: every block table begins with the
+    same ``shared_blocks`` physical blocks (stored once, read by all), then
+    each sequence's own cached tokens (uniform in [own_lo, own_hi]) and its new
+    tokens (uniform in [q_lo, q_hi]), which are the queries and are stored
+    through slot_mapping.  The logical K/V of every sequence begins with the
+    same prompt rows, so the oracle needs no knowledge of the sharing."""
+    g = _gen(seed)
+    S = shared_blocks * block_size
+    own = torch.randint(own_lo, own_hi + 1, (n_seqs,), generator=g).tolist()
+    lq = torch.randint(q_lo, q_hi + 1, (n_seqs,), generator=g).tolist()
+    lk = [S + o + q for o, q in zip(own, lq)]
+    base = varlen(lq, lk, hq, hkv, d, dtype, seed + 7)
+    cu = [int(x) for x in base.cu_seqlens_k.tolist()]
+    for b in range(1, n_seqs):                        # the same prompt in every sequence
+        base.k[cu[b]:cu[b] + S] = base.k[0:S]
+        base.v[cu[b]:cu[b] + S] = base.v[0:S]
+    own_blocks = [(L - S + block_size - 1) // block_size for L in lk]
+    num_blocks = shared_blocks + sum(own_blocks)
+    perm = torch.randperm(num_blocks, generator=g).to(torch.int32)
+    mbs = shared_blocks + max(own_blocks)
+    block_table = torch.full((n_seqs, mbs), -1, dtype=torch.int32)
+    pos = shared_blocks
+    for b in range(n_seqs):
+        block_table[b, :shared_blocks] = perm[:shared_blocks]
+        block_table[b, shared_blocks:shared_blocks + own_blocks[b]] = perm[pos:pos + own_blocks[b]]
+        pos += own_blocks[b]
+    k_cache = sentinel_like((num_blocks, block_size, hkv, d), dtype)
+    v_cache = sentinel_like((num_blocks, block_size, hkv, d), dtype)
+    j = torch.arange(S)
+    shared_phys = perm[:shared_blocks].to(torch.int64)[j // block_size]
+    k_cache[shared_phys, j % block_size] = base.k[0:S]
+    v_cache[shared_phys, j % block_size] = base.v[0:S]
+    new_rows, slots = [], []
+    for b in range(n_seqs):
+        jj = torch.arange(S, lk[b])
+        phys = block_table[b, jj // block_size].to(torch.int64)
+        off = jj % block_size
+        P = own[b]                                    # own cached tokens: positions S .. S + P
+        k_cache[phys[:P], off[:P]] = base.k[cu[b] + S:cu[b] + S + P]
+        v_cache[phys[:P], off[:P]] = base.v[cu[b] + S:cu[b] + S + P]
+        new_rows.append(torch.arange(cu[b] + S + P, cu[b] + lk[b]))
+        slots.append((phys[P:] * block_size + off[P:]).to(torch.int32))
+    rows = torch.cat(new_rows)
+    pg = Paged(k_cache, v_cache, block_table, base.k, base.v,
+               torch.as_tensor(cu, dtype=torch.int32), torch.as_tensor(lk, dtype=torch.int32),
+               torch.as_tensor([S + o for o in own], dtype=torch.int32),
+               base.k[rows].contiguous(), base.v[rows].contiguous(), torch.cat(slots),
+               block_size, mbs)
+    return PrefixPrefill(base.q, base.cu_seqlens_q, max(lq), max(lk), base.softmax_scale, pg,
+                         f"shared_prefix_{n_seqs}x({S}+[{own_lo},{own_hi}]+[{q_lo},{q_hi}])_bs{block_size}")
+
+
 @dataclass
 class Decode:
     """Single-token decode against a paged cache.  The cache holds the first
