@@ -25,42 +25,33 @@ int dtype_size(int dt) { return dt == ATTN_F32 ? 4 : (dt == ATTN_BF16 ? 2 : 0); 
 
 int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
-// Split size of the decode key range: the caller's (a positive multiple of
-// 64), or, for 0, one that gives the launch a few thousand workgroups.
-int resolve_split(int batch, int num_kv_heads, int max_blocks_per_seq, int block_size, int split) {
-    (void)batch;
-    (void)num_kv_heads;
-    if (split < 0 || split % 64 != 0) return -1;
-    if (split > 0) return split;
-    // the persistent split kernel balances whole splits across workgroups:
-    // 256 keys (one 64-key chunk per wavefront) keeps that balance fine
-    const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
-    int64_t s = 256;
-    if (s > cap) s = ((cap + 63) / 64) * 64;
-    return (int)s;
+// Keys per decode item: the caller's (a positive multiple of 32), or, for
+// 0, 32 -- one wavefront chunk, the finest grain the runs can be cut at.
+int resolve_split(int split) {
+    if (split < 0 || split % 32 != 0) return -1;
+    return split > 0 ? split : 32;
 }
 
+// Decode workspace: partial slots (kDecodeMaxRuns + batch) x hq of d fp32
+// values; then (256-aligned) 2 fp32 words per slot and head (m, d'); then
+// (256-aligned) two int32 per sequence (its first and last run).
 struct DecodeLayout {
     int split;
-    int max_splits;
-    size_t o_bytes;   // ws_o
-    size_t ml_off;    // ws_ml offset (256-aligned)
+    size_t ml_off;
+    size_t runs_off;
     size_t total;
 };
 
 bool decode_layout(int batch, int hq, int hkv, int d, int mbs, int bs, int split_req,
                    DecodeLayout *L) {
     if (batch <= 0 || hq <= 0 || hkv <= 0 || d <= 0 || mbs <= 0 || bs <= 0) return false;
-    const int split = resolve_split(batch, hkv, mbs, bs, split_req);
+    const int split = resolve_split(split_req);
     if (split <= 0) return false;
-    const int64_t cap = (int64_t)mbs * bs;
-    const int64_t ns = (cap + split - 1) / split;
-    const size_t rows = (size_t)batch * hq * (size_t)ns;
+    const size_t rows = ((size_t)attn::kDecodeMaxRuns + (size_t)batch) * (size_t)hq;
     L->split = split;
-    L->max_splits = (int)ns;
-    L->o_bytes = rows * (size_t)d * sizeof(float);
-    L->ml_off = (L->o_bytes + 255) / 256 * 256;
-    L->total = L->ml_off + rows * 4 * sizeof(float);   // m, d', split count, pad
+    L->ml_off = (rows * (size_t)d * sizeof(float) + 255) / 256 * 256;
+    L->runs_off = (L->ml_off + rows * 2 * sizeof(float) + 255) / 256 * 256;
+    L->total = L->runs_off + (size_t)batch * 2 * sizeof(int32_t);
     return true;
 }
 
@@ -184,14 +175,15 @@ ATTN_API int attn_decode_paged(const void *q, const void *k_cache, const void *v
     if (out_dtype != ATTN_F32 && out_dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
     if (num_q_heads / num_kv_heads > 16) return ATTN_ERR_UNSUPPORTED;
     if (block_size % 64 != 0) return ATTN_ERR_UNSUPPORTED;
-    if (split_tokens < 0 || split_tokens % 64 != 0) return ATTN_ERR_UNSUPPORTED;
+    if (split_tokens < 0 || split_tokens % 32 != 0) return ATTN_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
         return ATTN_ERR_UNSUPPORTED;
     DecodeLayout L;
     if (!decode_layout(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size,
                        split_tokens, &L))
         return ATTN_ERR_SHAPE;
-    if ((int64_t)batch * L.max_splits * num_kv_heads > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+    if ((int64_t)max_blocks_per_seq * block_size > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+    if ((int64_t)batch * num_q_heads * head_dim > 0x7fffffffLL) return ATTN_ERR_SHAPE;
     if (!workspace || workspace_bytes < L.total) return ATTN_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_ERR_WORKSPACE;
 
@@ -202,9 +194,14 @@ ATTN_API int attn_decode_paged(const void *q, const void *k_cache, const void *v
     a.max_blocks_per_seq = max_blocks_per_seq; a.num_blocks = num_blocks; a.block_size = block_size;
     a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
     a.split_tokens = L.split;
-    a.max_splits = L.max_splits;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return ATTN_ERR_HIP;
+    a.n_runs = attn::decode_runs(num_kv_heads, cus);
     a.ws_o = reinterpret_cast<float *>(workspace);
     a.ws_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + L.ml_off);
+    a.ws_runs = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(workspace) + L.runs_off);
     a.out_f32 = out_dtype == ATTN_F32;
     return hip_status(attn::launch_decode(a, (hipStream_t)stream));
 }

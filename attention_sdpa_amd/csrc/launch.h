@@ -40,6 +40,10 @@ struct VarlenArgs {
 hipError_t launch_prefill_f32(const VarlenArgs &a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const VarlenArgs &a, hipStream_t stream);
 
+// Persistent decode runs (one workgroup per CU and head block) are at most
+// this many; the workspace holds kDecodeMaxRuns + batch partial slots.
+constexpr int kDecodeMaxRuns = 1024;
+
 struct DecodeArgs {
     const void *q;
     const void *k_cache;
@@ -55,13 +59,16 @@ struct DecodeArgs {
     int num_blocks;
     int block_size;
     float scale_log2;
-    int split_tokens;  // resolved, > 0, multiple of 64
-    int max_splits;    // ceil(max_blocks_per_seq * block_size / split_tokens)
-    float *ws_o;       // [batch, hq, max_splits, d]
-    float *ws_ml;      // [batch, hq, max_splits, 4]: m, d', split count (int bits), pad
+    int split_tokens;  // keys per item, resolved, > 0, multiple of 32
+    int n_runs;        // runs the item stream is cut into, <= kDecodeMaxRuns
+    float *ws_o;       // [n_runs + batch slots, hq, d]
+    float *ws_ml;      // [n_runs + batch slots, hq, 2]: m (log2-scaled), d'
+    int32_t *ws_runs;  // [batch, 2]: runs holding each sequence's first and last item
     int out_f32;
 };
 
+// Runs of a decode launch on a device with `cus` compute units.
+int decode_runs(int hkv, int cus);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 
 }  // namespace attn

@@ -134,9 +134,13 @@ int attn_prefill_varlen(const void *q, const void *k, const void *v, void *o,
 
 /*
  * attn_decode_workspace_bytes -- bytes of device workspace attn_decode_paged
- * needs for these sizes (0 if the sizes are invalid): one fp32 partial row
- * of head_dim values plus 4 fp32 words (m, d', run length, pad) per
- * (sequence, query head, split).  split_tokens as in attn_decode_paged.
+ * needs for these sizes (0 if the sizes are invalid).  Layout: partial
+ * slots S = 1024 + batch, each with num_q_heads rows of head_dim fp32
+ * values; then, 256-byte aligned, 2 fp32 words per (slot, head) (m, d');
+ * then, 256-byte aligned, two int32 per sequence.  The size
+ * does not depend on max_blocks_per_seq, block_size or split_tokens, which
+ * are validated as in attn_decode_paged.  Nothing needs clearing between
+ * calls: every word the combine reads is written by the same call.
  */
 size_t attn_decode_workspace_bytes(int batch, int num_q_heads, int num_kv_heads,
                                    int head_dim, int max_blocks_per_seq,
@@ -154,14 +158,15 @@ size_t attn_decode_workspace_bytes(int batch, int num_q_heads, int num_kv_heads,
  * sequence the causal mask hides nothing.  L == 0 gives a zero row; L is
  * clipped to max_blocks_per_seq * block_size.
  *
- * The key range of each (sequence, KV head) is cut into splits of
- * split_tokens keys (0 = the library's choice, 256; else a positive
- * multiple of 64), which are dealt in equal contiguous runs to persistent
- * workgroups.  A workgroup keeps the online state (m, d', unnormalised o')
- * across the consecutive splits of one sequence it reads and stores one
- * partial per run; a second kernel merges the partials with the same
- * rescaling the online recurrence uses.  The result does not depend on
- * how the runs fall, up to floating-point rounding order.
+ * The keys of every sequence are cut into items of split_tokens keys (0 =
+ * the library's choice, 32; else a positive multiple of 32).  The items of
+ * all sequences, in order, are dealt in equal contiguous runs to persistent
+ * workgroups (one per compute unit), each serving every KV head of its
+ * keys.  A workgroup keeps the online state (m, d', unnormalised o') across
+ * the items of one sequence it reads and stores one partial per sequence it
+ * touches; a second kernel merges the partials with the same rescaling the
+ * online recurrence uses.  The result does not depend on how the runs fall,
+ * up to floating-point rounding order.
  *
  *   q             [batch, num_q_heads, head_dim], in_dtype
  *   k_cache,
@@ -175,6 +180,12 @@ size_t attn_decode_workspace_bytes(int batch, int num_q_heads, int num_kv_heads,
  *
  * Supported: in_dtype ATTN_BF16, head_dim 128, num_q_heads / num_kv_heads
  * <= 16, block_size a multiple of 64; out_dtype ATTN_F32 or ATTN_BF16.
+ * Errors: ATTN_ERR_NULL for a null pointer; ATTN_ERR_SHAPE for non-positive
+ * sizes, num_q_heads not a multiple of num_kv_heads or a bad scale;
+ * ATTN_ERR_UNSUPPORTED outside the supported set (also split_tokens not a
+ * multiple of 32, unaligned pointers); ATTN_ERR_WORKSPACE for a missing,
+ * small or unaligned workspace; ATTN_ERR_HIP if the device query or a
+ * launch fails.  Nothing is launched unless the status is ATTN_OK.
  */
 int attn_decode_paged(const void *q, const void *k_cache, const void *v_cache,
                       void *o, const int32_t *cache_seqlens,

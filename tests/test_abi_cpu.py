@@ -122,7 +122,7 @@ def test_decode_validation(lib):
     need = lib.attn_decode_workspace_bytes(4, 32, 8, 128, 32, 256, 0)
     assert need > 0
     assert lib.attn_decode_workspace_bytes(0, 32, 8, 128, 32, 256, 0) == 0
-    assert lib.attn_decode_workspace_bytes(4, 32, 8, 128, 32, 256, 100) == 0   # not a multiple of 64
+    assert lib.attn_decode_workspace_bytes(4, 32, 8, 128, 32, 256, 100) == 0   # not a multiple of 32
     assert decode(lib, bt=None) == E.ATTN_ERR_NULL
     assert decode(lib, B=0) == E.ATTN_ERR_SHAPE
     assert decode(lib, hq=12, hkv=8) == E.ATTN_ERR_SHAPE
@@ -132,15 +132,20 @@ def test_decode_validation(lib):
     assert decode(lib, hq=64, hkv=2) == E.ATTN_ERR_UNSUPPORTED   # group of 32 > 16
     assert decode(lib, bs=96) == E.ATTN_ERR_UNSUPPORTED
     assert decode(lib, split=100) == E.ATTN_ERR_UNSUPPORTED
+    assert decode(lib, split=48) == E.ATTN_ERR_UNSUPPORTED
     assert decode(lib, ws=None) == E.ATTN_ERR_WORKSPACE
     assert decode(lib, wsb=need - 1) == E.ATTN_ERR_WORKSPACE
     assert decode(lib, ws=MIS) == E.ATTN_ERR_WORKSPACE   # must be 256-byte aligned
-    # the workspace is exactly the documented partial layout: per (sequence,
-    # query head, split) d fp32 values, then (256-aligned) 4 fp32 words
-    def layout(batch, hq, d, mbs, bs, split):
-        rows = batch * hq * (-(-mbs * bs // split))
-        return (rows * d * 4 + 255) // 256 * 256 + rows * 16
-    for split in (64, 512, 1024):
-        assert lib.attn_decode_workspace_bytes(4, 32, 8, 128, 32, 256, split) == layout(4, 32, 128, 32, 256, split)
-    assert need == layout(4, 32, 128, 32, 256, 256)          # the default split is 256 keys
-    assert lib.attn_decode_workspace_bytes(2, 8, 8, 128, 1, 128, 0) == layout(2, 8, 128, 1, 128, 128)
+    # the workspace is exactly the documented layout: (1024 + batch) partial
+    # slots x hq rows of d fp32 values, then (256-aligned) 2 fp32 words per
+    # row, then (256-aligned) two int32 per sequence -- independent of the
+    # cache geometry and of the item size
+    def layout(batch, hq, d):
+        rows = (1024 + batch) * hq
+        ml = (rows * d * 4 + 255) // 256 * 256
+        runs = (ml + rows * 8 + 255) // 256 * 256
+        return runs + batch * 8
+    for split in (0, 32, 64, 512, 1024):
+        assert lib.attn_decode_workspace_bytes(4, 32, 8, 128, 32, 256, split) == layout(4, 32, 128)
+    assert need == layout(4, 32, 128)
+    assert lib.attn_decode_workspace_bytes(2, 8, 8, 128, 1, 128, 0) == layout(2, 8, 128)

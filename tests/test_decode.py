@@ -52,7 +52,7 @@ def test_decode_shapes_example():
     check_bf16(np32(got), oracle_decode(dc), "decode [2,32,128]")
 
 
-@pytest.mark.parametrize("split", [0, 64, 256, 1024])
+@pytest.mark.parametrize("split", [0, 32, 64, 256, 1024])
 def test_decode_ragged_contexts(split):
     ctx = [1, 2, 63, 64, 65, 255, 256, 257, 1000, 3000]
     dc = make_decode(ctx, seed=7)
@@ -60,11 +60,29 @@ def test_decode_ragged_contexts(split):
     check_bf16(np32(run_decode(dc, split)), oracle_decode(dc), f"decode split {split}")
 
 
-@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 1), (12, 4)])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 1), (12, 4), (12, 3), (32, 16), (24, 12), (10, 5)])
 def test_decode_group_sizes(hq, hkv):
     dc = make_decode([17, 700, 129], hq=hq, hkv=hkv, block_size=64, seed=hq + hkv)
     log(f"case decode groups {hq}/{hkv}")
     check_bf16(np32(run_decode(dc)), oracle_decode(dc), f"decode {hq}/{hkv}")
+
+
+@pytest.mark.parametrize("split", [0, 96])
+def test_decode_many_short_sequences(split):
+    """More sequences than a wavefront scans at once and than there are
+    compute units, most far shorter than one run, with empty ones between:
+    runs then hold many sequences each and the partial links are short."""
+    rng = np.random.default_rng(11)
+    ctx = [int(c) for c in rng.integers(0, 120, size=300)]
+    ctx[5] = ctx[77] = ctx[299] = 0
+    ctx[130] = 2000
+    dc = make_decode(ctx, hq=16, hkv=4, block_size=64, seed=12)
+    log(f"case decode 300 short sequences split={split}")
+    got = np32(run_decode(dc, split))
+    ref = oracle_decode(dc)
+    for b in (5, 77, 299):
+        assert np.all(got[b] == 0)
+    check_bf16(got, ref, f"decode 300 short split {split}")
 
 
 def test_decode_zero_context_and_bf16_output():
