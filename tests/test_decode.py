@@ -139,3 +139,23 @@ def test_decode_shared_prefix_blocks():
     log("case decode shared prefix blocks")
     for split in (0, 256):
         check_bf16(np32(run_decode(dc, split)), oracle_decode(dc), f"decode shared prefix split {split}")
+
+
+def test_decode_reused_workspace():
+    """One workspace serves calls of different sizes back to back: every word
+    the merge reads is written by the same call, so nothing needs clearing
+    (it starts as garbage here on purpose)."""
+    cases = [make_decode([5000, 3000, 700], seed=21), make_decode([9000], seed=22),
+             make_decode([64, 1, 4000, 2500, 0, 128], seed=23), make_decode([5000, 3000, 700], seed=24)]
+    need = max(attn.attn_decode_workspace_bytes(dc.q.shape[0], 32, 8, 128,
+                                                dc.paged.block_table.shape[1], 256, 0) for dc in cases)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")
+    for i, dc in enumerate(cases * 2):
+        pg = dc.paged
+        kc, vc = dev(pg.k_cache), dev(pg.v_cache)
+        attn.kv_store_slots(dev(pg.k_new), dev(pg.v_new), kc, vc, dev(pg.slot_mapping))
+        got = attn.attn_decode_paged(dev(dc.q), kc, vc, dev(pg.seqlens_k), dev(pg.block_table),
+                                     dc.softmax_scale, workspace=ws, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        log(f"case decode reused workspace call {i}")
+        check_bf16(np32(got), oracle_decode(dc), f"decode reused workspace call {i}")
