@@ -22,7 +22,8 @@ ATTN_F32, ATTN_BF16 = 0, 1
 
 # exported C symbols (kept in sync with include/attn.h by the CPU tests)
 SYMBOLS = ("attn_status_str", "attn_version", "kv_store_slots", "attn_prefill_varlen",
-           "attn_decode_workspace_bytes", "attn_decode_paged")
+           "attn_decode_workspace_bytes", "attn_decode_paged", "attn_unfused_workspace_bytes",
+           "attn_prefill_unfused")
 
 
 class AttnError(RuntimeError):
@@ -62,6 +63,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, i32p, i32p, ci, ci, ci, ci, ci, ci, ci, cf,
                                       ci, ci, ci, vp, csz, vp]
     lib.attn_decode_paged.restype = ci
+    lib.attn_unfused_workspace_bytes.argtypes = [ci, ci, ci, ci]
+    lib.attn_unfused_workspace_bytes.restype = csz
+    lib.attn_prefill_unfused.argtypes = [vp, vp, vp, vp, i32p, i32p, ci, ci, ci, ci, ci, ci, ci, ci,
+                                         cf, ci, ci, ci, vp, csz, vp]
+    lib.attn_prefill_unfused.restype = ci
     if path is None:
         _lib = lib
     return lib
@@ -169,4 +175,32 @@ def attn_decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _i32(cache_seqlens), _i32(block_table),
         B, hq, hkv, d, mbs, nb, bs, float(softmax_scale), int(split_tokens), _dt(q), _dt(out),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def attn_unfused_workspace_bytes(batch: int, num_q_heads: int, max_seqlen_q: int, max_seqlen_k: int) -> int:
+    return int(load_library().attn_unfused_workspace_bytes(batch, num_q_heads, max_seqlen_q, max_seqlen_k))
+
+
+def attn_prefill_unfused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                         cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
+                         max_seqlen_q: int, max_seqlen_k: int, softmax_scale: float,
+                         causal: bool = True, workspace: Optional[torch.Tensor] = None,
+                         out: Optional[torch.Tensor] = None, out_dtype=None, stream=None) -> torch.Tensor:
+    """The unfused three-kernel baseline (X and A through HBM); arguments as
+    attn_prefill_varlen with contiguous K/V."""
+    total_q, hq, d = q.shape
+    total_k, hkv = k.shape[0], k.shape[1]
+    B = cu_seqlens_q.numel() - 1
+    if out is None:
+        out = torch.empty((total_q, hq, d), dtype=out_dtype or q.dtype, device=q.device)
+    need = attn_unfused_workspace_bytes(B, hq, max_seqlen_q, max_seqlen_k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    lib = load_library()
+    _check("attn_prefill_unfused", lib.attn_prefill_unfused(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _i32(cu_seqlens_q), _i32(cu_seqlens_k), B,
+        int(max_seqlen_q), int(max_seqlen_k), total_q, total_k, hq, hkv, d, float(softmax_scale),
+        int(bool(causal)), _dt(q), _dt(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
     return out

@@ -205,3 +205,69 @@ ATTN_API int attn_decode_paged(const void *q, const void *k_cache, const void *v
     a.out_f32 = out_dtype == ATTN_F32;
     return hip_status(attn::launch_decode(a, (hipStream_t)stream));
 }
+
+namespace {
+
+// Unfused-baseline workspace: X fp32 then (256-aligned) A bf16, each
+// [batch, hq, max_seqlen_q, ldx] with ldx = max_seqlen_k rounded up to 64,
+// plus 64 (rows a power-of-two apart would fall on the same few memory
+// channels when a wavefront writes 32 of them at once).
+bool unfused_layout(int batch, int hq, int max_q, int max_k, int64_t *ldx, size_t *a_off, size_t *total) {
+    if (batch <= 0 || hq <= 0 || max_q < 0 || max_k < 0) return false;
+    const int64_t l = ((int64_t)max_k + 63) / 64 * 64 + 64;
+    const size_t elems = (size_t)batch * hq * (size_t)max_q * (size_t)l;
+    *ldx = l;
+    *a_off = (elems * sizeof(float) + 255) / 256 * 256;
+    *total = *a_off + elems * 2;
+    return true;
+}
+
+}  // namespace
+
+ATTN_API size_t attn_unfused_workspace_bytes(int batch, int num_q_heads, int max_seqlen_q,
+                                             int max_seqlen_k) {
+    int64_t ldx;
+    size_t a_off, total;
+    if (!unfused_layout(batch, num_q_heads, max_seqlen_q, max_seqlen_k, &ldx, &a_off, &total)) return 0;
+    return total;
+}
+
+ATTN_API int attn_prefill_unfused(const void *q, const void *k, const void *v, void *o,
+                                  const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                                  int batch, int max_seqlen_q, int max_seqlen_k,
+                                  int total_q, int total_k, int num_q_heads, int num_kv_heads,
+                                  int head_dim, float softmax_scale, int causal, int in_dtype,
+                                  int out_dtype, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+    if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_k) return ATTN_ERR_NULL;
+    if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seqlen_q < 0 ||
+        max_seqlen_k < 0 || total_q < 0 || total_k < 0)
+        return ATTN_ERR_SHAPE;
+    if (num_q_heads % num_kv_heads != 0) return ATTN_ERR_SHAPE;
+    if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return ATTN_ERR_SHAPE;
+    if (in_dtype != ATTN_BF16 || head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+    if (out_dtype != ATTN_F32 && out_dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if ((int64_t)batch * num_q_heads > 65535) return ATTN_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_UNSUPPORTED;
+    int64_t ldx;
+    size_t a_off, total;
+    if (!unfused_layout(batch, num_q_heads, max_seqlen_q, max_seqlen_k, &ldx, &a_off, &total))
+        return ATTN_ERR_SHAPE;
+    if (!workspace || workspace_bytes < total) return ATTN_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_ERR_WORKSPACE;
+    if (total_q == 0) return ATTN_OK;
+
+    attn::UnfusedArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o;
+    a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
+    a.batch = batch; a.max_seqlen_q = max_seqlen_q; a.max_seqlen_k = max_seqlen_k;
+    a.total_q = total_q; a.total_k = total_k;
+    a.hq = num_q_heads; a.hkv = num_kv_heads;
+    a.scale = softmax_scale;
+    a.causal = causal ? 1 : 0;
+    a.x = reinterpret_cast<float *>(workspace);
+    a.a = reinterpret_cast<char *>(workspace) + a_off;
+    a.ldx = ldx;
+    a.out_f32 = out_dtype == ATTN_F32;
+    return hip_status(attn::launch_unfused(a, (hipStream_t)stream));
+}

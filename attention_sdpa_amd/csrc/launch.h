@@ -71,4 +71,30 @@ struct DecodeArgs {
 int decode_runs(int hkv, int cus);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 
+// The unfused three-step baseline (logits, softmax and A V as separate
+// kernels with X and A in the workspace).
+struct UnfusedArgs {
+    const void *q;
+    const void *k;
+    const void *v;
+    void *o;
+    const int32_t *cu_q;
+    const int32_t *cu_k;
+    int batch;
+    int max_seqlen_q;
+    int max_seqlen_k;
+    int total_q;
+    int total_k;
+    int hq;
+    int hkv;
+    float scale;       // softmax_scale
+    int causal;
+    float *x;          // [batch, hq, max_seqlen_q, ldx] fp32 logits
+    void *a;           // [batch, hq, max_seqlen_q, ldx] bf16 probabilities
+    int64_t ldx;       // max_seqlen_k rounded up to 64
+    int out_f32;
+};
+
+hipError_t launch_unfused(const UnfusedArgs &a, hipStream_t stream);
+
 }  // namespace attn

@@ -18,6 +18,9 @@ the paged cache (kv_store_slots), then attention.
   cached K and V byte read once per KV head; GB/s.
 * roofline: the prefill kernel alone, from events recorded around each of
   its launches inside the timed region, against bf16 dense MFMA peak.
+* unfused_baseline: the blog's standard three-step method (X and A stored in
+  HBM between three kernels) on the same varlen workload, next to the fused
+  kernel's time; skipped with --skip-unfused (it needs ~52 GB of workspace).
 * cpu_baseline: the fp64 CPU oracle timed on a bounded sample of the same
   workload's rows on this host's cores, scaled to TFLOP/s by the same
   algorithmic flop count.
@@ -192,6 +195,46 @@ def bench_decode(args, torch, attn, workloads):
                 gbs_kernel=kv_bytes / (k_ms * 1e-3) / 1e9)
 
 
+def bench_unfused(args, torch, attn, workloads, fused_ms):
+    """The unfused three-kernel baseline (X and A stored in HBM between the
+    steps) on the headline varlen workload, next to the fused kernel."""
+    vl = workloads.varlen_prefill()
+    q, k, v = vl.q.cuda(), vl.k.cuda(), vl.v.cuda()
+    cu_q, cu_k = vl.cu_seqlens_q.cuda(), vl.cu_seqlens_k.cuda()
+    out = torch.empty_like(q)
+    B = vl.cu_seqlens_q.numel() - 1
+    need = attn.attn_unfused_workspace_bytes(B, 32, vl.max_seqlen_q, vl.max_seqlen_k)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    Ev = torch.cuda.Event
+
+    def step(i):
+        e0, e1 = Ev(enable_timing=True), Ev(enable_timing=True)
+        e0.record()
+        attn.attn_prefill_unfused(q, k, v, cu_q, cu_k, vl.max_seqlen_q, vl.max_seqlen_k,
+                                  vl.softmax_scale, True, workspace=ws, out=out)
+        e1.record()
+        return e0, e1
+
+    steps, warmup = max(1, min(args.steps, 10)), max(1, min(args.warmup, 2))
+    _, kms = timed_loop(step, steps, warmup, torch)
+    ms = sum(kms) / len(kms)
+    lq = (vl.cu_seqlens_q[1:] - vl.cu_seqlens_q[:-1]).tolist()
+    lk = (vl.cu_seqlens_k[1:] - vl.cu_seqlens_k[:-1]).tolist()
+    pairs_all = float(sum(a * b for a, b in zip(lq, lk)))
+    # X written (fp32) and read back, A written (bf16) and read back, per
+    # (query, key) pair and query head: the round trips the fused kernel avoids
+    xa_bytes = pairs_all * 32 * (4 + 4 + 2 + 2)
+    pairs = visible_pairs(vl.cu_seqlens_q.tolist(), vl.cu_seqlens_k.tolist(), True)
+    flops = 4.0 * 128 * 32 * pairs
+    del ws
+    return {"workload": "the headline varlen causal prefill, unfused: X = s*QK^T (fp32) and "
+                        "A = softmax(X) (bf16) stored in HBM between three kernels",
+            "kernel_ms": round(ms, 4), "steps": steps,
+            "tflops_alg": round(flops / (ms * 1e-3) / 1e12, 2),
+            "xa_bytes": xa_bytes, "xa_gbs": round(xa_bytes / (ms * 1e-3) / 1e9, 1),
+            "fused_kernel_ms": round(fused_ms, 4), "fused_speedup": round(ms / fused_ms, 2)}
+
+
 def host_threads() -> int:
     """CPU threads this process may use (its affinity mask, capped by
     OMP_NUM_THREADS when that is set)."""
@@ -245,7 +288,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
-    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "unfused"], default="all")
+    ap.add_argument("--skip-unfused", action="store_true",
+                    help="omit the unfused three-kernel baseline (it needs ~52 GB of workspace)")
     ap.add_argument("--prefill-workload", choices=["varlen", "long", "noncausal"], default="varlen",
                     help="prefill workload to time: the varlen 16-sequence batch (headline), the "
                          "32768-token single sequence, or the varlen batch without the causal mask")
@@ -285,6 +330,14 @@ def main():
         print(f"[bench] prefill step {pre['ms_step']:.3f} ms, kernel {pre['kernel_ms']:.3f} ms, "
               f"{pre['tflops_kernel']:.1f} TFLOP/s kernel", file=sys.stderr, flush=True)
         res["prefill"] = pre
+    if args.only in ("all", "prefill", "unfused") and args.prefill_workload == "varlen" and \
+            not args.skip_unfused:
+        fused_ms = res["prefill"]["kernel_ms"] if "prefill" in res else float("nan")
+        unf = bench_unfused(args, torch, attn, workloads, fused_ms)
+        print(f"[bench] unfused baseline {unf['kernel_ms']:.3f} ms "
+              f"(fused kernel {fused_ms:.3f} ms), X/A traffic {unf['xa_gbs']:.0f} GB/s",
+              file=sys.stderr, flush=True)
+        res["unfused"] = unf
     if args.only in ("all", "decode"):
         dec = bench_decode(args, torch, attn, workloads)
         print(f"[bench] decode step {dec['ms_step']:.3f} ms, kernels {dec['kernel_ms']:.3f} ms, "
@@ -331,6 +384,8 @@ def main():
             line.update({"value": dobj["value"], "unit": "GB/s", "ms_per_step": dobj["ms_per_step"],
                          "config": {"workload": dobj["workload"]},
                          "roofline": dobj["roofline"]})
+    if "unfused" in res:
+        line["unfused_baseline"] = res["unfused"]
     if not args.skip_cpu and "prefill" in res:
         line["cpu_baseline"] = cpu_baseline_prefill(res["prefill"]["vl"], args.cpu_seconds)
     print(json.dumps(line), flush=True)

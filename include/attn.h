@@ -195,6 +195,47 @@ int attn_decode_paged(const void *q, const void *k_cache, const void *v_cache,
                       int split_tokens, int in_dtype, int out_dtype,
                       void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * attn_unfused_workspace_bytes -- bytes of device workspace
+ * attn_prefill_unfused needs (0 if the sizes are invalid): the logits X as
+ * fp32, then (256-byte aligned) the probabilities A as bf16, each laid out
+ * [batch, num_q_heads, max_seqlen_q, ldx] with ldx = max_seqlen_k rounded
+ * up to a multiple of 64, plus 64.
+ */
+size_t attn_unfused_workspace_bytes(int batch, int num_q_heads, int max_seqlen_q,
+                                    int max_seqlen_k);
+
+/*
+ * attn_prefill_unfused -- the page's standard, unfused method (section
+ * 标准实现方法) as a measured baseline for attn_prefill_varlen: three kernels,
+ *     X = softmax_scale * Q K^T          (written to the workspace, fp32)
+ *     A = softmax(X) row by row          (3-pass safe softmax, masked keys
+ *                                         get weight 0; written as bf16)
+ *     O = A V
+ * with the same arguments, semantics (varlen packing, GQA, end-aligned
+ * causal mask, zero rows for queries with no visible key) and output as
+ * attn_prefill_varlen with block_table == NULL.  X and A are formed for
+ * every (query, key) pair of each sequence, as the standard method does, so
+ * they cost HBM traffic of about 12 bytes per pair and head.
+ *
+ *   workspace    at least attn_unfused_workspace_bytes(batch, num_q_heads,
+ *                max_seqlen_q, max_seqlen_k) bytes, 256-byte aligned;
+ *                contents on entry are ignored
+ *
+ * Supported: in_dtype ATTN_BF16, head_dim 128, contiguous K/V, out_dtype
+ * ATTN_F32 or ATTN_BF16, batch * num_q_heads <= 65535, 16-byte aligned
+ * pointers.  Errors as attn_prefill_varlen, plus ATTN_ERR_WORKSPACE for a
+ * missing, small or unaligned workspace.  Nothing is launched unless the
+ * status is ATTN_OK.  Asynchronous on stream; allocates nothing.
+ */
+int attn_prefill_unfused(const void *q, const void *k, const void *v, void *o,
+                         const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                         int batch, int max_seqlen_q, int max_seqlen_k,
+                         int total_q, int total_k, int num_q_heads, int num_kv_heads,
+                         int head_dim, float softmax_scale, int causal, int in_dtype,
+                         int out_dtype, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
 #ifdef __cplusplus
 }
 #endif

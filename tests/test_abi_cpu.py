@@ -149,3 +149,41 @@ def test_decode_validation(lib):
         assert lib.attn_decode_workspace_bytes(4, 32, 8, 128, 32, 256, split) == layout(4, 32, 128)
     assert need == layout(4, 32, 128)
     assert lib.attn_decode_workspace_bytes(2, 8, 8, 128, 1, 128, 0) == layout(2, 8, 128)
+
+
+def unfused(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, cu_q=P2, cu_k=P2, batch=2, maxq=16, maxk=16, total_q=20,
+             total_k=20, hq=32, hkv=8, d=128, scale=0.088, causal=1, idt=attn.ATTN_BF16,
+             odt=attn.ATTN_F32, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return lib.attn_prefill_unfused(a["q"], a["k"], a["v"], a["o"], a["cu_q"], a["cu_k"], a["batch"],
+                                    a["maxq"], a["maxk"], a["total_q"], a["total_k"], a["hq"], a["hkv"],
+                                    a["d"], a["scale"], a["causal"], a["idt"], a["odt"], a["ws"],
+                                    a["wsb"], None)
+
+
+def test_unfused_validation(lib):
+    E = attn
+    # X fp32 then (256-aligned) A bf16, each [batch, hq, max_q, ldx], ldx = max_k
+    # rounded up to 64, plus 64
+    def layout(batch, hq, mq, mk):
+        elems = batch * hq * mq * (-(-mk // 64) * 64 + 64)
+        return (elems * 4 + 255) // 256 * 256 + elems * 2
+    for args in ((2, 32, 16, 16), (3, 8, 100, 65), (1, 1, 4096, 4096), (16, 32, 4096, 4096)):
+        assert lib.attn_unfused_workspace_bytes(*args) == layout(*args)
+    assert lib.attn_unfused_workspace_bytes(0, 32, 16, 16) == 0
+    need = layout(2, 32, 16, 16)
+    assert unfused(lib, wsb=need) != E.ATTN_ERR_WORKSPACE or False   # enough: fails later only for want of a GPU
+    assert unfused(lib, q=None) == E.ATTN_ERR_NULL
+    assert unfused(lib, cu_k=None) == E.ATTN_ERR_NULL
+    assert unfused(lib, batch=0) == E.ATTN_ERR_SHAPE
+    assert unfused(lib, hq=12, hkv=8) == E.ATTN_ERR_SHAPE
+    assert unfused(lib, scale=float("nan")) == E.ATTN_ERR_SHAPE
+    assert unfused(lib, idt=E.ATTN_F32) == E.ATTN_ERR_UNSUPPORTED
+    assert unfused(lib, d=64) == E.ATTN_ERR_UNSUPPORTED
+    assert unfused(lib, odt=7) == E.ATTN_ERR_UNSUPPORTED
+    assert unfused(lib, batch=4096, hq=32, hkv=8) == E.ATTN_ERR_UNSUPPORTED   # grid limit
+    assert unfused(lib, o=MIS) == E.ATTN_ERR_UNSUPPORTED
+    assert unfused(lib, ws=None) == E.ATTN_ERR_WORKSPACE
+    assert unfused(lib, wsb=need - 1) == E.ATTN_ERR_WORKSPACE
+    assert unfused(lib, ws=MIS) == E.ATTN_ERR_WORKSPACE
