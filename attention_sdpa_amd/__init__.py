@@ -23,7 +23,7 @@ ATTN_F32, ATTN_BF16 = 0, 1
 # exported C symbols (kept in sync with include/attn.h by the CPU tests)
 SYMBOLS = ("attn_status_str", "attn_version", "kv_store_slots", "attn_prefill_varlen",
            "attn_decode_workspace_bytes", "attn_decode_paged", "attn_unfused_workspace_bytes",
-           "attn_prefill_unfused")
+           "attn_prefill_unfused", "attn_prefill_padded")
 
 
 class AttnError(RuntimeError):
@@ -63,6 +63,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, i32p, i32p, ci, ci, ci, ci, ci, ci, ci, cf,
                                       ci, ci, ci, vp, csz, vp]
     lib.attn_decode_paged.restype = ci
+    lib.attn_prefill_padded.argtypes = [vp, vp, vp, vp, i32p, i32p, ci, ci, ci, ci, ci, ci, cf, ci, ci,
+                                        ci, vp]
+    lib.attn_prefill_padded.restype = ci
     lib.attn_unfused_workspace_bytes.argtypes = [ci, ci, ci, ci]
     lib.attn_unfused_workspace_bytes.restype = csz
     lib.attn_prefill_unfused.argtypes = [vp, vp, vp, vp, i32p, i32p, ci, ci, ci, ci, ci, ci, ci, ci,
@@ -203,4 +206,21 @@ def attn_prefill_unfused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         int(max_seqlen_q), int(max_seqlen_k), total_q, total_k, hq, hkv, d, float(softmax_scale),
         int(bool(causal)), _dt(q), _dt(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+    return out
+
+
+def attn_prefill_padded(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seqlens_q: torch.Tensor,
+                        seqlens_k: torch.Tensor, softmax_scale: float, causal: bool = True,
+                        out: Optional[torch.Tensor] = None, out_dtype=None, stream=None) -> torch.Tensor:
+    """Prefill on a padded batch: q [B, Lq_max, Hq, d], k/v [B, Lk_max, Hkv, d],
+    seqlens_q/seqlens_k [B] int32.  Output rows at or past seqlens_q[b] are
+    left as they are in `out` (zeros when `out` is omitted)."""
+    B, mq, hq, d = q.shape
+    mk, hkv = k.shape[1], k.shape[2]
+    if out is None:
+        out = torch.zeros((B, mq, hq, d), dtype=out_dtype or q.dtype, device=q.device)
+    lib = load_library()
+    _check("attn_prefill_padded", lib.attn_prefill_padded(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _i32(seqlens_q), _i32(seqlens_k), B, mq, mk, hq, hkv, d,
+        float(softmax_scale), int(bool(causal)), _dt(q), _dt(out), _stream(stream)))
     return out

@@ -143,6 +143,61 @@ ATTN_API int attn_prefill_varlen(const void *q, const void *k, const void *v, vo
     a.num_blocks = paged ? num_blocks : 0;
     a.block_size = paged ? block_size : 0;
     a.out_f32 = out_dtype == ATTN_F32;
+    a.seqlens_q = nullptr;
+    a.seqlens_k = nullptr;
+    a.pad_q = 0;
+    a.pad_k = 0;
+    const hipError_t e = (in_dtype == ATTN_BF16) ? attn::launch_prefill_bf16(a, (hipStream_t)stream)
+                                                 : attn::launch_prefill_f32(a, (hipStream_t)stream);
+    return hip_status(e);
+}
+
+ATTN_API int attn_prefill_padded(const void *q, const void *k, const void *v, void *o,
+                                 const int32_t *seqlens_q, const int32_t *seqlens_k,
+                                 int batch, int max_seqlen_q, int max_seqlen_k,
+                                 int num_q_heads, int num_kv_heads, int head_dim,
+                                 float softmax_scale, int causal, int in_dtype, int out_dtype,
+                                 void *stream) {
+    if (!q || !k || !v || !o || !seqlens_q || !seqlens_k) return ATTN_ERR_NULL;
+    if (batch <= 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+        head_dim <= 0)
+        return ATTN_ERR_SHAPE;
+    if (num_q_heads % num_kv_heads != 0) return ATTN_ERR_SHAPE;
+    if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return ATTN_ERR_SHAPE;
+    if (out_dtype != ATTN_F32 && out_dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (in_dtype == ATTN_BF16) {
+        if (head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+    } else if (in_dtype == ATTN_F32) {
+        if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+    } else {
+        return ATTN_ERR_UNSUPPORTED;
+    }
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_UNSUPPORTED;
+    const int64_t total_q = (int64_t)batch * max_seqlen_q, total_k = (int64_t)batch * max_seqlen_k;
+    if (total_q > 0x7fffffffLL || total_k > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+    const int64_t units = ((int64_t)max_seqlen_q + 31) / 32 * batch * num_q_heads;
+    if (units > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+    if (max_seqlen_q == 0) return ATTN_OK;
+
+    attn::VarlenArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o;
+    a.cu_q = nullptr; a.cu_k = nullptr;
+    a.block_table = nullptr;
+    a.batch = batch;
+    a.max_seqlen_q = max_seqlen_q;
+    a.total_q = total_q;
+    a.total_k = total_k;
+    a.hq = num_q_heads; a.hkv = num_kv_heads; a.d = head_dim;
+    a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+    a.causal = causal ? 1 : 0;
+    a.max_blocks_per_seq = 0;
+    a.num_blocks = 0;
+    a.block_size = 0;
+    a.out_f32 = out_dtype == ATTN_F32;
+    a.seqlens_q = seqlens_q;
+    a.seqlens_k = seqlens_k;
+    a.pad_q = max_seqlen_q;
+    a.pad_k = max_seqlen_k;   // 0: every sequence has no key
     const hipError_t e = (in_dtype == ATTN_BF16) ? attn::launch_prefill_bf16(a, (hipStream_t)stream)
                                                  : attn::launch_prefill_f32(a, (hipStream_t)stream);
     return hip_status(e);

@@ -35,6 +35,14 @@ struct VarlenArgs {
     int num_blocks;
     int block_size;
     int out_f32;  // 1: fp32 output, 0: bf16 output
+    // Padded batches: pad_q > 0 places sequence b's queries at rows
+    // b * pad_q .. with seqlens_q[b] of them, and its keys at rows
+    // b * pad_k .. with min(seqlens_k[b], pad_k) of them (cu_q, cu_k and
+    // block_table unused).  pad_q == 0: the varlen layout of cu_q / cu_k.
+    const int32_t *seqlens_q;
+    const int32_t *seqlens_k;
+    int pad_q;
+    int pad_k;
 };
 
 hipError_t launch_prefill_f32(const VarlenArgs &a, hipStream_t stream);

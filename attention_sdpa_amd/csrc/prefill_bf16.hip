@@ -156,11 +156,23 @@ struct SeqMeta {
 
 __device__ __forceinline__ SeqMeta seq_meta(const VarlenArgs &a, int b) {
     SeqMeta m;
-    int q0 = ld_meta(a.cu_q, b), q1 = ld_meta(a.cu_q, b + 1);
-    q0 = q0 < 0 ? 0 : (q0 > a.total_q ? (int)a.total_q : q0);
-    q1 = q1 < q0 ? q0 : (q1 > a.total_q ? (int)a.total_q : q1);
-    m.q0 = q0;
-    m.Lq = q1 - q0;
+    if (a.pad_q) {   // padded batch: rows b * pad_q .., seqlens_q[b] of them
+        const int L = ld_meta(a.seqlens_q, b);
+        m.q0 = b * a.pad_q;
+        m.Lq = L < 0 ? 0 : (L > a.pad_q ? a.pad_q : L);
+    } else {
+        int q0 = ld_meta(a.cu_q, b), q1 = ld_meta(a.cu_q, b + 1);
+        q0 = q0 < 0 ? 0 : (q0 > a.total_q ? (int)a.total_q : q0);
+        q1 = q1 < q0 ? q0 : (q1 > a.total_q ? (int)a.total_q : q1);
+        m.q0 = q0;
+        m.Lq = q1 - q0;
+    }
+    if (a.pad_q) {
+        const int L = ld_meta(a.seqlens_k, b);
+        m.k0 = b * a.pad_k;
+        m.Lk = L < 0 ? 0 : (L > a.pad_k ? a.pad_k : L);
+        return m;
+    }
     int k0 = ld_meta(a.cu_k, b), k1 = ld_meta(a.cu_k, b + 1);
     if (a.block_table) {
         k1 = k1 < k0 ? k0 : k1;

@@ -42,17 +42,33 @@ prefill_f32_kernel(VarlenArgs a, int nqt) {
     const int b = id % a.batch;
     const int qt = nqt - 1 - id / a.batch;
 
-    int64_t q0 = a.cu_q[b], q1 = a.cu_q[b + 1];
-    q0 = q0 < 0 ? 0 : (q0 > a.total_q ? a.total_q : q0);
-    q1 = q1 < q0 ? q0 : (q1 > a.total_q ? a.total_q : q1);
+    int64_t q0, q1;
+    if (a.pad_q) {   // padded batch: rows b * pad_q .., seqlens_q[b] of them
+        const int L = a.seqlens_q[b];
+        q0 = (int64_t)b * a.pad_q;
+        q1 = q0 + (L < 0 ? 0 : (L > a.pad_q ? a.pad_q : L));
+    } else {
+        q0 = a.cu_q[b];
+        q1 = a.cu_q[b + 1];
+        q0 = q0 < 0 ? 0 : (q0 > a.total_q ? a.total_q : q0);
+        q1 = q1 < q0 ? q0 : (q1 > a.total_q ? a.total_q : q1);
+    }
     const int Lq = (int)(q1 - q0);
-    int64_t k0 = a.cu_k[b], k1 = a.cu_k[b + 1];
+    int64_t k0 = 0, k1 = 0;
     int Lk;
-    if (a.block_table) {
+    if (a.pad_q) {
+        const int L = a.seqlens_k[b];
+        k0 = (int64_t)b * a.pad_k;
+        Lk = L < 0 ? 0 : (L > a.pad_k ? a.pad_k : L);
+    } else if (a.block_table) {
+        k0 = a.cu_k[b];
+        k1 = a.cu_k[b + 1];
         k1 = k1 < k0 ? k0 : k1;
         const int64_t cap = (int64_t)a.max_blocks_per_seq * a.block_size;
         Lk = (int)((k1 - k0) > cap ? cap : (k1 - k0));
     } else {
+        k0 = a.cu_k[b];
+        k1 = a.cu_k[b + 1];
         k0 = k0 < 0 ? 0 : (k0 > a.total_k ? a.total_k : k0);
         k1 = k1 < k0 ? k0 : (k1 > a.total_k ? a.total_k : k1);
         Lk = (int)(k1 - k0);

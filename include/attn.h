@@ -133,6 +133,34 @@ int attn_prefill_varlen(const void *q, const void *k, const void *v, void *o,
                         int in_dtype, int out_dtype, void *stream);
 
 /*
+ * attn_prefill_padded -- the same attention as attn_prefill_varlen for a
+ * padded batch (the page's Prefill section contrasts the padded layout of
+ * a batch with its varlen packing by cu_seqlens; the two give the same
+ * outputs on the valid rows).  Sequence b holds seqlens_q[b] queries at
+ * rows 0 .. of q[b] and seqlens_k[b] keys at rows 0 .. of k[b] and v[b]
+ * (lengths are clipped to [0, max_seqlen_*]); the causal mask is aligned to
+ * the sequence end as in attn_prefill_varlen.  Padded rows are not read as
+ * keys, and output rows at or past seqlens_q[b] are left unchanged.  The
+ * varlen kernels run in place on the padded tensors: nothing is packed or
+ * copied.
+ *
+ *   q, o           [batch, max_seqlen_q, num_q_heads, head_dim]
+ *   k, v           [batch, max_seqlen_k, num_kv_heads, head_dim]
+ *   seqlens_q,
+ *   seqlens_k      [batch] int32 device arrays
+ *
+ * Supported: as attn_prefill_varlen with contiguous K/V; batch *
+ * max_seqlen_q and batch * max_seqlen_k below 2^31.  Errors as
+ * attn_prefill_varlen.
+ */
+int attn_prefill_padded(const void *q, const void *k, const void *v, void *o,
+                        const int32_t *seqlens_q, const int32_t *seqlens_k,
+                        int batch, int max_seqlen_q, int max_seqlen_k,
+                        int num_q_heads, int num_kv_heads, int head_dim,
+                        float softmax_scale, int causal, int in_dtype, int out_dtype,
+                        void *stream);
+
+/*
  * attn_decode_workspace_bytes -- bytes of device workspace attn_decode_paged
  * needs for these sizes (0 if the sizes are invalid).  Layout: partial
  * slots S = 1024 + batch, each with num_q_heads rows of head_dim fp32

@@ -187,3 +187,28 @@ def test_unfused_validation(lib):
     assert unfused(lib, ws=None) == E.ATTN_ERR_WORKSPACE
     assert unfused(lib, wsb=need - 1) == E.ATTN_ERR_WORKSPACE
     assert unfused(lib, ws=MIS) == E.ATTN_ERR_WORKSPACE
+
+
+def padded(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lq=P2, lk=P2, batch=2, maxq=16, maxk=16, hq=32, hkv=8, d=128,
+             scale=0.088, causal=1, idt=attn.ATTN_BF16, odt=attn.ATTN_F32)
+    a.update(kw)
+    return lib.attn_prefill_padded(a["q"], a["k"], a["v"], a["o"], a["lq"], a["lk"], a["batch"],
+                                   a["maxq"], a["maxk"], a["hq"], a["hkv"], a["d"], a["scale"],
+                                   a["causal"], a["idt"], a["odt"], None)
+
+
+def test_padded_validation(lib):
+    E = attn
+    assert padded(lib, lq=None) == E.ATTN_ERR_NULL
+    assert padded(lib, v=None) == E.ATTN_ERR_NULL
+    assert padded(lib, batch=0) == E.ATTN_ERR_SHAPE
+    assert padded(lib, maxq=-1) == E.ATTN_ERR_SHAPE
+    assert padded(lib, hq=12, hkv=8) == E.ATTN_ERR_SHAPE
+    assert padded(lib, scale=-0.5) == E.ATTN_ERR_SHAPE
+    assert padded(lib, batch=1 << 20, maxq=1 << 12) == E.ATTN_ERR_SHAPE      # rows past 2^31
+    assert padded(lib, d=64) == E.ATTN_ERR_UNSUPPORTED                       # bf16 needs 128
+    assert padded(lib, idt=E.ATTN_F32, d=96) == E.ATTN_ERR_UNSUPPORTED
+    assert padded(lib, odt=5) == E.ATTN_ERR_UNSUPPORTED
+    assert padded(lib, k=MIS) == E.ATTN_ERR_UNSUPPORTED
+    assert padded(lib, maxq=0) == E.ATTN_OK                                  # nothing to do
