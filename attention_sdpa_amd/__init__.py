@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libattn.so")
 
 ATTN_OK, ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(6)
-ATTN_F32, ATTN_BF16 = 0, 1
+ATTN_F32, ATTN_BF16, ATTN_F16 = 0, 1, 2
 
 # exported C symbols (kept in sync with include/attn.h by the CPU tests)
 SYMBOLS = ("attn_status_str", "attn_version", "kv_store_slots", "attn_prefill_varlen",
@@ -87,6 +87,8 @@ def _dt(t: torch.Tensor) -> int:
         return ATTN_BF16
     if t.dtype == torch.float32:
         return ATTN_F32
+    if t.dtype == torch.float16:
+        return ATTN_F16
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 

@@ -21,7 +21,9 @@ constexpr int kVersion = 10000;  // 1.0.0
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int dtype_size(int dt) { return dt == ATTN_F32 ? 4 : (dt == ATTN_BF16 ? 2 : 0); }
+int dtype_size(int dt) { return dt == ATTN_F32 ? 4 : ((dt == ATTN_BF16 || dt == ATTN_F16) ? 2 : 0); }
+
+bool is16(int dt) { return dt == ATTN_BF16 || dt == ATTN_F16; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
@@ -113,12 +115,13 @@ ATTN_API int attn_prefill_varlen(const void *q, const void *k, const void *v, vo
     } else if (total_k < 0) {
         return ATTN_ERR_SHAPE;
     }
-    if (out_dtype != ATTN_F32 && out_dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-    if (in_dtype == ATTN_BF16) {
+    if (is16(in_dtype)) {
         if (head_dim != 128) return ATTN_ERR_UNSUPPORTED;
         if (paged && block_size % 64 != 0) return ATTN_ERR_UNSUPPORTED;
+        if (out_dtype != ATTN_F32 && out_dtype != in_dtype) return ATTN_ERR_UNSUPPORTED;
     } else if (in_dtype == ATTN_F32) {
         if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+        if (out_dtype != ATTN_F32 && out_dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
     } else {
         return ATTN_ERR_UNSUPPORTED;
     }
@@ -147,8 +150,9 @@ ATTN_API int attn_prefill_varlen(const void *q, const void *k, const void *v, vo
     a.seqlens_k = nullptr;
     a.pad_q = 0;
     a.pad_k = 0;
-    const hipError_t e = (in_dtype == ATTN_BF16) ? attn::launch_prefill_bf16(a, (hipStream_t)stream)
-                                                 : attn::launch_prefill_f32(a, (hipStream_t)stream);
+    a.in_f16 = in_dtype == ATTN_F16;
+    const hipError_t e = is16(in_dtype) ? attn::launch_prefill_mfma(a, (hipStream_t)stream)
+                                        : attn::launch_prefill_f32(a, (hipStream_t)stream);
     return hip_status(e);
 }
 
@@ -164,11 +168,12 @@ ATTN_API int attn_prefill_padded(const void *q, const void *k, const void *v, vo
         return ATTN_ERR_SHAPE;
     if (num_q_heads % num_kv_heads != 0) return ATTN_ERR_SHAPE;
     if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return ATTN_ERR_SHAPE;
-    if (out_dtype != ATTN_F32 && out_dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-    if (in_dtype == ATTN_BF16) {
+    if (is16(in_dtype)) {
         if (head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+        if (out_dtype != ATTN_F32 && out_dtype != in_dtype) return ATTN_ERR_UNSUPPORTED;
     } else if (in_dtype == ATTN_F32) {
         if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+        if (out_dtype != ATTN_F32 && out_dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
     } else {
         return ATTN_ERR_UNSUPPORTED;
     }
@@ -198,8 +203,9 @@ ATTN_API int attn_prefill_padded(const void *q, const void *k, const void *v, vo
     a.seqlens_k = seqlens_k;
     a.pad_q = max_seqlen_q;
     a.pad_k = max_seqlen_k;   // 0: every sequence has no key
-    const hipError_t e = (in_dtype == ATTN_BF16) ? attn::launch_prefill_bf16(a, (hipStream_t)stream)
-                                                 : attn::launch_prefill_f32(a, (hipStream_t)stream);
+    a.in_f16 = in_dtype == ATTN_F16;
+    const hipError_t e = is16(in_dtype) ? attn::launch_prefill_mfma(a, (hipStream_t)stream)
+                                        : attn::launch_prefill_f32(a, (hipStream_t)stream);
     return hip_status(e);
 }
 
@@ -226,8 +232,8 @@ ATTN_API int attn_decode_paged(const void *q, const void *k_cache, const void *v
         return ATTN_ERR_SHAPE;
     if (num_q_heads % num_kv_heads != 0) return ATTN_ERR_SHAPE;
     if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return ATTN_ERR_SHAPE;
-    if (in_dtype != ATTN_BF16 || head_dim != 128) return ATTN_ERR_UNSUPPORTED;
-    if (out_dtype != ATTN_F32 && out_dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (!is16(in_dtype) || head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+    if (out_dtype != ATTN_F32 && out_dtype != in_dtype) return ATTN_ERR_UNSUPPORTED;
     if (num_q_heads / num_kv_heads > 16) return ATTN_ERR_UNSUPPORTED;
     if (block_size % 64 != 0) return ATTN_ERR_UNSUPPORTED;
     if (split_tokens < 0 || split_tokens % 32 != 0) return ATTN_ERR_UNSUPPORTED;
@@ -258,6 +264,7 @@ ATTN_API int attn_decode_paged(const void *q, const void *k_cache, const void *v
     a.ws_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + L.ml_off);
     a.ws_runs = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(workspace) + L.runs_off);
     a.out_f32 = out_dtype == ATTN_F32;
+    a.in_f16 = in_dtype == ATTN_F16;
     return hip_status(attn::launch_decode(a, (hipStream_t)stream));
 }
 

@@ -33,7 +33,7 @@
 //   several wavefronts share a head).  K and V rows go by direct
 //   global->LDS loads (four whole 256-byte rows per instruction) into
 //   per-wavefront buffers.  K comes back by 16-byte reads as the A operand
-//   of S^T = K Q^T (v_mfma_f32_16x16x32_bf16, keys = M, query heads = N);
+//   of S^T = K Q^T (v_mfma_f32_16x16x32_bf16 or _f16, keys = M, query heads = N);
 //   V comes back by transposing reads (ds_read_b64_tr_b16) as the A operand
 //   of O^T += V^T P^T.  Both are read into registers before any arithmetic,
 //   and the next chunk's K and V loads are issued into the same buffers
@@ -72,9 +72,11 @@ __host__ __device__ __forceinline__ int heads_per_block(int hkv) {
     return hkv >= 8 ? 8 : (hkv > 4 ? 8 : (hkv > 2 ? 4 : hkv));
 }
 
-template <int D>
+template <typename T, int D>
 __global__ void __launch_bounds__(kDecThreads, 1)
 decode_split_kernel(DecodeArgs a) {
+    typedef typename Vec16<T>::x4 T4;
+    typedef typename Vec16<T>::x8 T8;
     constexpr int KK = D / 32;          // k-steps of 32 over head_dim
     constexpr int DB = D / 16;          // 16-row blocks of d in O^T
     constexpr int MB = kChunk / 16;     // 16-key row blocks of a chunk
@@ -158,7 +160,7 @@ decode_split_kernel(DecodeArgs a) {
     const int n_items = __builtin_amdgcn_readfirstlane(sStart[2]);
     if (n_items <= 0 || b >= a.batch) return;
 
-    bf16x8 qf[KK];
+    T8 qf[KK];
     f32x4 o[DB];
     float m_run, mc_run, l_run;
     const float cl = a.scale_log2;
@@ -220,7 +222,7 @@ decode_split_kernel(DecodeArgs a) {
             }
         // V^T operands by transposing reads: for MFMA (jj, db) a lane holds
         // 8 keys of one d, the key order matching P's
-        bf16x8 vf[JJ][DB];
+        T8 vf[JJ][DB];
 #pragma unroll
         for (int jj = 0; jj < JJ; ++jj)
 #pragma unroll
@@ -230,8 +232,8 @@ decode_split_kernel(DecodeArgs a) {
                 const int ch = col >> 3, sub = col & 7;
                 const bf16 *p0 = vbuf + r0 * D + ((ch ^ swz_dv(r0)) * 8) + sub;
                 const bf16 *p1 = vbuf + (r0 + 16) * D + ((ch ^ swz_dv(r0 + 16)) * 8) + sub;
-                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ATTN_LDS bf16x4 *)p0);
-                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ATTN_LDS bf16x4 *)p1);
+                const T4 lo = ds_read_tr4<T>(p0);
+                const T4 hi = ds_read_tr4<T>(p1);
                 vf[jj][db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             }
         // both buffers are read: the next chunk's loads go out now and stay
@@ -249,8 +251,7 @@ decode_split_kernel(DecodeArgs a) {
             sacc[mb] = f32x4{};
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk)
-                sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    *reinterpret_cast<bf16x8 *>(&kr[mb][kk]), qf[kk], sacc[mb], 0, 0, 0);
+                sacc[mb] = mfma_16x16x32(*reinterpret_cast<T8 *>(&kr[mb][kk]), qf[kk], sacc[mb]);
         }
         // mask keys past the segment end: lane holds keys 16mb + 4gq + i
         const int last = kend - 1 - c0;
@@ -272,14 +273,14 @@ decode_split_kernel(DecodeArgs a) {
         const float mc_new = (m_new == kNegInf) ? 0.f : m_new * cl;
         const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2(mc_run - mc_new);
         float psum = 0.f;
-        bf16x8 pb[JJ];
+        T8 pb[JJ];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float p = fast_exp2(fmaf(sacc[mb][i], cl, -mc_new));
                 psum += p;
-                pb[mb >> 1][4 * (mb & 1) + i] = f32_to_bf16(p);
+                pb[mb >> 1][4 * (mb & 1) + i] = to16<T>(p);
             }
         l_run = l_run * alpha + psum;
         m_run = m_new;
@@ -291,7 +292,7 @@ decode_split_kernel(DecodeArgs a) {
         for (int jj = 0; jj < JJ; ++jj)
 #pragma unroll
             for (int db = 0; db < DB; ++db)
-                o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[jj][db], pb[jj], o[db], 0, 0, 0);
+                o[db] = mfma_16x16x32(vf[jj][db], pb[jj], o[db]);
     };
 
     // merge the waves' states of one head (wpH waves per head) for the
@@ -366,7 +367,7 @@ decode_split_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk) {
                     uint4 t = qv ? ld16(qp + 32 * kk) : make_uint4(0, 0, 0, 0);
-                    qf[kk] = *reinterpret_cast<bf16x8 *>(&t);
+                    qf[kk] = *reinterpret_cast<T8 *>(&t);
                 }
             }
             const int blk0 = blk_of(b, c0);
@@ -395,7 +396,7 @@ decode_split_kernel(DecodeArgs a) {
     }
 }
 
-template <int D>
+template <typename T, int D>
 __global__ void __launch_bounds__(D)
 decode_combine_kernel(DecodeArgs a) {
     constexpr int kBatchLoads = 4;  // partials read together
@@ -444,7 +445,7 @@ decode_combine_kernel(DecodeArgs a) {
     if (a.out_f32)
         ((float *)a.o)[(int64_t)bh * D + d] = res;
     else
-        ((bf16 *)a.o)[(int64_t)bh * D + d] = f32_to_bf16(res);
+        ((T *)a.o)[(int64_t)bh * D + d] = to16<T>(res);
 }
 
 }  // namespace
@@ -458,18 +459,23 @@ int decode_runs(int hkv, int cus) {
     return runs;
 }
 
-hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+template <typename T>
+hipError_t launch_decode_typed(const DecodeArgs &a, hipStream_t stream) {
     constexpr int D = 128;
     if (a.batch == 0) return hipSuccess;
     const int hb = heads_per_block(a.hkv);
     const int nb = (a.hkv + hb - 1) / hb;
     // one persistent workgroup per (run, head block)
     const int64_t grid = (int64_t)a.n_runs * nb;
-    hipLaunchKernelGGL(decode_split_kernel<D>, dim3((unsigned)grid), dim3(kDecThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3((unsigned)grid), dim3(kDecThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((unsigned)(a.batch * a.hq)), dim3(D), 0, stream, a);
+    hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)(a.batch * a.hq)), dim3(D), 0, stream, a);
     return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+    return a.in_f16 ? launch_decode_typed<f16>(a, stream) : launch_decode_typed<bf16>(a, stream);
 }
 
 }  // namespace attn

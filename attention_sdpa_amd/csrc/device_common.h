@@ -10,6 +10,10 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -28,6 +32,44 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
 
 // Round-to-nearest-even float -> bf16 (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ bf16 f32_to_bf16(float x) { return (bf16)x; }
+
+// ---- the two 16-bit input types (bf16, fp16) ---------------------------
+// Vectors of a 16-bit element type, and the matrix-core instructions and
+// conversions that go with it.  Data move as raw 16-bit values (LDS copies,
+// transposing LDS reads), so only arithmetic needs the type.
+template <typename T> struct Vec16;
+template <> struct Vec16<bf16> { typedef bf16x2 x2; typedef bf16x4 x4; typedef bf16x8 x8; };
+template <> struct Vec16<f16> { typedef f16x2 x2; typedef f16x4 x4; typedef f16x8 x8; };
+
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_32x32x16(f16x8 a, f16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_16x16x32(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+// c + a.x * b.x + a.y * b.y with fp32 accumulation (v_dot2_f32_*)
+__device__ __forceinline__ float dot2_acc(bf16x2 a, bf16x2 b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+__device__ __forceinline__ float dot2_acc(f16x2 a, f16x2 b, float c) {
+    return __builtin_amdgcn_fdot2(a, b, c, false);
+}
+// Round-to-nearest-even float -> T.
+template <typename T>
+__device__ __forceinline__ T to16(float x) { return (T)x; }
+
+// Transposing LDS read of 4 16-bit values (ds_read_b64_tr_b16), as T.
+template <typename T>
+__device__ __forceinline__ typename Vec16<T>::x4 ds_read_tr4(const void *p) {
+    const bf16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ATTN_LDS bf16x4 *)(p));
+    return __builtin_bit_cast(typename Vec16<T>::x4, r);
+}
 
 // Value held by lane (lane ^ 32): exchanges the two 32-lane halves.
 __device__ __forceinline__ float swap_halves(float x) {

@@ -34,7 +34,8 @@ struct VarlenArgs {
     int max_blocks_per_seq;
     int num_blocks;
     int block_size;
-    int out_f32;  // 1: fp32 output, 0: bf16 output
+    int out_f32;  // 1: fp32 output, 0: output in the 16-bit input type
+    int in_f16;   // 16-bit inputs: 1 fp16, 0 bf16
     // Padded batches: pad_q > 0 places sequence b's queries at rows
     // b * pad_q .. with seqlens_q[b] of them, and its keys at rows
     // b * pad_k .. with min(seqlens_k[b], pad_k) of them (cu_q, cu_k and
@@ -46,7 +47,8 @@ struct VarlenArgs {
 };
 
 hipError_t launch_prefill_f32(const VarlenArgs &a, hipStream_t stream);
-hipError_t launch_prefill_bf16(const VarlenArgs &a, hipStream_t stream);
+// bf16 or fp16 inputs (VarlenArgs::in_f16) on the matrix cores
+hipError_t launch_prefill_mfma(const VarlenArgs &a, hipStream_t stream);
 
 // Persistent decode runs (one workgroup per CU and head block) are at most
 // this many; the workspace holds kDecodeMaxRuns + batch partial slots.
@@ -72,7 +74,8 @@ struct DecodeArgs {
     float *ws_o;       // [n_runs + batch slots, hq, d]
     float *ws_ml;      // [n_runs + batch slots, hq, 2]: m (log2-scaled), d'
     int32_t *ws_runs;  // [batch, 2]: runs holding each sequence's first and last item
-    int out_f32;
+    int out_f32;       // 1: fp32 output, 0: output in the input type
+    int in_f16;        // 1: fp16 inputs, 0: bf16
 };
 
 // Runs of a decode launch on a device with `cus` compute units.

@@ -1,4 +1,6 @@
-// prefill_bf16.hip -- fused varlen causal prefill on the gfx950 matrix cores.
+// prefill_mfma.hip -- fused varlen causal prefill on the gfx950 matrix cores,
+// for bf16 or fp16 inputs (the kernel is a template on the 16-bit type; P
+// is rounded to the same type for the P V product).
 //
 // Algorithm: the FlashAttention one-pass recurrence of the blog post
 // "从零实现 vLLM (1.3)：如何加速 Attention 计算" (sections FlashAttention 的最终
@@ -289,9 +291,12 @@ struct WaveView {
     bool row_valid;
 };
 
-template <bool kListed>
+template <typename T, bool kListed>
 __global__ void __launch_bounds__(kThreads, 1)
-prefill_bf16_kernel(VarlenArgs a, Geo geo) {
+prefill_mfma_kernel(VarlenArgs a, Geo geo) {
+    typedef typename Vec16<T>::x2 T2;
+    typedef typename Vec16<T>::x4 T4;
+    typedef typename Vec16<T>::x8 T8;
     constexpr int KK = kD / 16;         // MFMA k-steps over head_dim
     constexpr int DB = kD / 32;         // 32-row blocks of d in O^T
     constexpr int kStageBytes = kTileElems * 2;
@@ -554,11 +559,11 @@ prefill_bf16_kernel(VarlenArgs a, Geo geo) {
     if (!grpA) issue();
 
     int st = 0;                                            // ring stage of the unit's first tile
-    bf16x8 qf[KK];
+    T8 qf[KK];
     f32x16 o[DB];
     float m_ref, mc_ref, l_run;
     f32x16 sacc[2];
-    bf16x8 pb[4];
+    T8 pb[4];
     // Q rows of unit u into qf.  A row past the sequence end reads the
     // sequence's first row instead: finite values confined to its own lane
     // pair, whose output is dropped.
@@ -568,7 +573,7 @@ prefill_bf16_kernel(VarlenArgs a, Geo geo) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             uint4 tq = ld16(qp + 16 * kk);
-            qf[kk] = *reinterpret_cast<bf16x8 *>(&tq);
+            qf[kk] = *reinterpret_cast<T8 *>(&tq);
         }
     };
     // O = o' / d' of unit u.  Buffer stores against a resource that spans
@@ -605,11 +610,11 @@ prefill_bf16_kernel(VarlenArgs a, Geo geo) {
             for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int pr = 0; pr < 2; ++pr) {
-                    bf16x4 y, x;
+                    T4 y, x;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        y[e] = f32_to_bf16(o[db][8 * pr + e] * inv);
-                        x[e] = f32_to_bf16(o[db][8 * pr + 4 + e] * inv);
+                        y[e] = to16<T>(o[db][8 * pr + e] * inv);
+                        x[e] = to16<T>(o[db][8 * pr + 4 + e] * inv);
                     }
                     const u32x2 yu = *reinterpret_cast<u32x2 *>(&y), xu = *reinterpret_cast<u32x2 *>(&x);
                     const auto s0 = __builtin_amdgcn_permlane32_swap(yu[0], xu[0], false, false);
@@ -629,7 +634,7 @@ prefill_bf16_kernel(VarlenArgs a, Geo geo) {
 #pragma unroll
         for (int i = 0; i < DB; ++i) o[i] = f32x16{};
         m_ref = kNegInf; mc_ref = 0.f; l_run = 0.f;
-        const bf16x2 ones2 = {(bf16)1.f, (bf16)1.f};
+        const T2 ones2 = {(T)1.f, (T)1.f};
         const int k_row = perm23(n);
         const int gq = lane >> 4, s16 = lane & 15;
         const int v_row_part = 8 * (gq >> 1) + (s16 >> 2);
@@ -645,8 +650,8 @@ prefill_bf16_kernel(VarlenArgs a, Geo geo) {
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk) {
                     const int ch = (2 * kk + hf) ^ (lane & 15);
-                    const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(krow + ch * 8);
-                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[kb], 0, 0, 0);
+                    const T8 kf = *reinterpret_cast<const T8 *>(krow + ch * 8);
+                    sacc[kb] = mfma_32x32x16(kf, qf[kk], sacc[kb]);
                 }
             }
             __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
@@ -667,12 +672,12 @@ prefill_bf16_kernel(VarlenArgs a, Geo geo) {
             constexpr int kAhead = 4;
             const bf16 *Kt = &sK[0][0] + ks * kTileElems;
             const bf16 *Vt = &sV[0][0] + vs * kTileElems;
-            bf16x8 kbuf[16], vbuf[16];
+            T8 kbuf[16], vbuf[16];
             auto read_k = [&](int i) ATTN_INLINE {
                 const int kb = i >> 3, kk = i & 7;
                 const bf16 *krow = Kt + (32 * kb + k_row) * kD;
                 const int ch = (2 * kk + hf) ^ (lane & 15);
-                kbuf[i] = *reinterpret_cast<const bf16x8 *>(krow + ch * 8);
+                kbuf[i] = *reinterpret_cast<const T8 *>(krow + ch * 8);
             };
             auto read_v = [&](int i) ATTN_INLINE {
                 const int jj = i >> 2, db = i & 3;
@@ -681,8 +686,8 @@ prefill_bf16_kernel(VarlenArgs a, Geo geo) {
                 const int ch0 = col >> 3, sub = col & 7;
                 const bf16 *p0r = Vt + r * kD + ((ch0 ^ swz_v(r)) * 8) + sub;
                 const bf16 *p1r = Vt + (r + 4) * kD + ((ch0 ^ swz_v(r + 4)) * 8) + sub;
-                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ATTN_LDS bf16x4 *)(p0r));
-                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ATTN_LDS bf16x4 *)(p1r));
+                const T4 lo = ds_read_tr4<T>(p0r);
+                const T4 hi = ds_read_tr4<T>(p1r);
                 vbuf[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             };
 #pragma unroll
@@ -698,16 +703,16 @@ prefill_bf16_kernel(VarlenArgs a, Geo geo) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 if constexpr (kQK) {
-                    sacc[i >> 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kbuf[i], qf[i & 7], sacc[i >> 3], 0, 0, 0);
+                    sacc[i >> 3] = mfma_32x32x16(kbuf[i], qf[i & 7], sacc[i >> 3]);
                     if (i + kAhead < 16) read_k(i + kAhead);
                 }
                 const int jj = i >> 2, db = i & 3;
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vbuf[i], pb[jj], o[db], 0, 0, 0);
+                o[db] = mfma_32x32x16(vbuf[i], pb[jj], o[db]);
                 if (i + kAhead < 16) read_v(i + kAhead);
-                bf16x2 pr;
+                T2 pr;
                 pr[0] = pb[jj][2 * db];
                 pr[1] = pb[jj][2 * db + 1];
-                l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, l_run, false);
+                l_run = dot2_acc(pr, ones2, l_run);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
@@ -751,12 +756,12 @@ prefill_bf16_kernel(VarlenArgs a, Geo geo) {
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
-                    pb[2 * kb + (i >> 3)][i & 7] = f32_to_bf16(fast_exp2(fmaf(sacc[kb][i], cl, -mc_ref)));
+                    pb[2 * kb + (i >> 3)][i & 7] = to16<T>(fast_exp2(fmaf(sacc[kb][i], cl, -mc_ref)));
         };
 
         auto zero_p = [&]() ATTN_INLINE {
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) pb[jj] = bf16x8{};
+            for (int jj = 0; jj < 4; ++jj) pb[jj] = T8{};
         };
 
         // ---- prologue: S^T and P of the unit's first tile ------------------
@@ -826,7 +831,8 @@ prefill_bf16_kernel(VarlenArgs a, Geo geo) {
 
 }  // namespace
 
-hipError_t launch_prefill_bf16(const VarlenArgs &a, hipStream_t stream) {
+template <typename T>
+hipError_t launch_prefill_typed(const VarlenArgs &a, hipStream_t stream) {
     const int group = a.hq / a.hkv;
     Geo geo;
     geo.hpw = (group % 4 == 0) ? 4 : (group % 2 == 0 ? 2 : 1);
@@ -853,15 +859,19 @@ hipError_t launch_prefill_bf16(const VarlenArgs &a, hipStream_t stream) {
     const bool listed = a.batch <= kMaxBatchListed && geo.nqt <= kMaxRowsListed && a.hkv <= 256 &&
                         geo.head_chunks <= 256 && (units_max + grid_l - 1) / grid_l <= kMaxUnitsListed;
     if (listed) {
-        hipLaunchKernelGGL(prefill_bf16_kernel<true>, dim3((unsigned)grid_l), dim3(kThreads), 0, stream, a, geo);
+        hipLaunchKernelGGL((prefill_mfma_kernel<T, true>), dim3((unsigned)grid_l), dim3(kThreads), 0, stream, a, geo);
     } else {
         // a multiple of the padded KV-head count keeps each workgroup on one head
         int64_t grid = geo.slots < (int64_t)cus ? geo.slots : (int64_t)cus;
         const int g2 = 1 << geo.lg;
         if (grid > g2) grid -= grid % g2;
-        hipLaunchKernelGGL(prefill_bf16_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a, geo);
+        hipLaunchKernelGGL((prefill_mfma_kernel<T, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a, geo);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_prefill_mfma(const VarlenArgs &a, hipStream_t stream) {
+    return a.in_f16 ? launch_prefill_typed<f16>(a, stream) : launch_prefill_typed<bf16>(a, stream);
 }
 
 }  // namespace attn

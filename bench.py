@@ -43,7 +43,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 # Sources whose hash identifies each kernel; a recorded HBM-traffic figure is
 # reported only while these files are unchanged since the counters were taken.
 KERNEL_SOURCES = {
-    "prefill": ["attention_sdpa_amd/csrc/prefill_bf16.hip", "attention_sdpa_amd/csrc/device_common.h",
+    "prefill": ["attention_sdpa_amd/csrc/prefill_mfma.hip", "attention_sdpa_amd/csrc/device_common.h",
                 "attention_sdpa_amd/csrc/launch.h"],
     "decode": ["attention_sdpa_amd/csrc/decode.hip", "attention_sdpa_amd/csrc/device_common.h",
                "attention_sdpa_amd/csrc/launch.h"],
@@ -362,7 +362,7 @@ def main():
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(pre["tflops_kernel"] / PEAK_BF16_TFLOPS, 4),
                          "traffic": recorded_traffic("prefill"),
-                         "kernel": "prefill_bf16_kernel<128>",
+                         "kernel": "prefill_mfma_kernel<bf16>",
                          "kernel_ms": round(pre["kernel_ms"], 4)},
         })
     if "decode" in res:

@@ -28,7 +28,8 @@
  *   block id outside [0, num_blocks) reads as a zero row, a slot outside the
  *   cache is skipped, and a sequence range outside [0, total) is clipped, so
  *   bad metadata gives wrong numbers, never an out-of-bounds access.
- * - dtype codes: ATTN_F32 (IEEE binary32) and ATTN_BF16 (bfloat16).
+ * - dtype codes: ATTN_F32 (IEEE binary32), ATTN_BF16 (bfloat16) and ATTN_F16
+ *   (IEEE binary16).
  * - Grouped-query attention: query head h reads KV head h / (Hq / Hkv).
  */
 #ifndef ATTN_MI355X_ATTN_H
@@ -50,7 +51,7 @@ enum attn_status {
     ATTN_ERR_HIP = 5          /* the HIP runtime reported an error              */
 };
 
-enum attn_dtype { ATTN_F32 = 0, ATTN_BF16 = 1 };
+enum attn_dtype { ATTN_F32 = 0, ATTN_BF16 = 1, ATTN_F16 = 2 };
 
 /* Status code -> static, human-readable string (never NULL). */
 const char *attn_status_str(int status);
@@ -73,7 +74,7 @@ int attn_version(void);
  *   v_cache       [num_blocks, block_size, num_kv_heads, head_dim], dtype
  *   slot_mapping  [num_tokens] int32; slots must be distinct (two tokens
  *                 writing one slot race and the result is either of them)
- *   dtype         ATTN_BF16 or ATTN_F32
+ *   dtype         ATTN_BF16, ATTN_F16 or ATTN_F32 (rows are copied bit for bit)
  * num_tokens == 0 is a no-op returning ATTN_OK.
  */
 int kv_store_slots(const void *k, const void *v, void *k_cache, void *v_cache,
@@ -116,9 +117,11 @@ int kv_store_slots(const void *k, const void *v, void *k_cache, void *v_cache,
  *                is rejected with ATTN_ERR_SHAPE
  *   causal       nonzero = causal mask as above
  *
- * Supported: in_dtype ATTN_BF16 with head_dim 128 (bf16 matrix cores, fp32
- * softmax state) and in_dtype ATTN_F32 with head_dim 64 or 128 (fp32
- * throughout); out_dtype ATTN_F32 or ATTN_BF16 (round to nearest even);
+ * Supported: in_dtype ATTN_BF16 or ATTN_F16 with head_dim 128 (16-bit
+ * matrix cores, P rounded to the input type, fp32 softmax state; out_dtype
+ * ATTN_F32 or the input type) and in_dtype ATTN_F32 with head_dim 64 or 128
+ * (fp32 throughout; out_dtype ATTN_F32 or ATTN_BF16); conversions round to
+ * nearest even;
  * num_q_heads a multiple of num_kv_heads; block_size a multiple of 64 when
  * paged.  Pointers must be 16-byte aligned.
  */
@@ -206,8 +209,9 @@ size_t attn_decode_workspace_bytes(int batch, int num_q_heads, int num_kv_heads,
  *   workspace     device scratch of at least attn_decode_workspace_bytes()
  *                 bytes, 256-byte aligned, not shared with a concurrent call
  *
- * Supported: in_dtype ATTN_BF16, head_dim 128, num_q_heads / num_kv_heads
- * <= 16, block_size a multiple of 64; out_dtype ATTN_F32 or ATTN_BF16.
+ * Supported: in_dtype ATTN_BF16 or ATTN_F16, head_dim 128, num_q_heads /
+ * num_kv_heads <= 16, block_size a multiple of 64; out_dtype ATTN_F32 or
+ * the input type.
  * Errors: ATTN_ERR_NULL for a null pointer; ATTN_ERR_SHAPE for non-positive
  * sizes, num_q_heads not a multiple of num_kv_heads or a bad scale;
  * ATTN_ERR_UNSUPPORTED outside the supported set (also split_tokens not a

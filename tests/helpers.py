@@ -95,3 +95,33 @@ def sample_rows(cu_q: torch.Tensor, hq: int, n: int, seed: int) -> np.ndarray:
     if total > 0:
         rows.extend((rng.integers(0, total, n) * hq + rng.integers(0, hq, n)).tolist())
     return np.unique(np.asarray(rows, dtype=np.int64))
+
+
+# fp16 inputs: the kernels round P to fp16 (relative error <= 2^-11 per
+# weight, doubled at most by the normalisation) and accumulate in fp32, so
+# with |V| <= ~5.5 the output error is below 2 * 2^-11 * 5.5 ~ 5.4e-3; the
+# bar is half the bf16 one.
+F16_MAX_ABS = 5e-3
+F16_MEAN_ABS = 5e-4
+
+
+def check_f16(got, ref, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    mx, mean = errs(got, ref)
+    log(f"  {what}: fp16 max abs {mx:.3e} mean abs {mean:.3e}")
+    assert mx <= F16_MAX_ABS, f"{what}: max abs {mx:.3e} > {F16_MAX_ABS}"
+    assert mean <= F16_MEAN_ABS, f"{what}: mean abs {mean:.3e} > {F16_MEAN_ABS}"
+
+
+def check_f16_output(got_f16: torch.Tensor, ref, what=""):
+    """fp16-valued output vs the oracle rounded to fp16 (RNE)."""
+    ref = np.asarray(ref, dtype=np.float64)
+    ref_h = ref.astype(np.float16).astype(np.float64)
+    got = got_f16.detach().double().cpu().numpy()
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    mag = np.maximum(np.abs(ref_h), 2.0 ** -14)
+    ulp = 2.0 ** (np.floor(np.log2(mag)) - 10)      # fp16: 11 significant bits
+    excess = np.abs(got - ref_h) - (F16_MAX_ABS + ulp)
+    log(f"  {what}: fp16-out max |diff| {np.abs(got - ref_h).max():.3e}")
+    assert np.all(excess <= 0), f"{what}: fp16 output outside 5e-3 + 1 ulp"

@@ -212,3 +212,19 @@ def test_padded_validation(lib):
     assert padded(lib, odt=5) == E.ATTN_ERR_UNSUPPORTED
     assert padded(lib, k=MIS) == E.ATTN_ERR_UNSUPPORTED
     assert padded(lib, maxq=0) == E.ATTN_OK                                  # nothing to do
+
+
+def test_fp16_validation(lib):
+    """fp16 inputs go to the 16-bit matrix-core kernels; the output is fp32
+    or the input type (fp16 in, bf16 out is not a supported pair)."""
+    E = attn
+    assert E.ATTN_F16 == 2
+    assert prefill(lib, idt=E.ATTN_F16, odt=E.ATTN_BF16) == E.ATTN_ERR_UNSUPPORTED
+    assert prefill(lib, idt=E.ATTN_BF16, odt=E.ATTN_F16) == E.ATTN_ERR_UNSUPPORTED
+    assert prefill(lib, idt=E.ATTN_F16, d=64) == E.ATTN_ERR_UNSUPPORTED
+    assert prefill(lib, idt=E.ATTN_F32, odt=E.ATTN_F16) == E.ATTN_ERR_UNSUPPORTED
+    assert decode(lib, idt=E.ATTN_F16, odt=E.ATTN_BF16) == E.ATTN_ERR_UNSUPPORTED
+    assert decode(lib, idt=E.ATTN_BF16, odt=E.ATTN_F16) == E.ATTN_ERR_UNSUPPORTED
+    assert padded(lib, idt=E.ATTN_F16, odt=E.ATTN_BF16) == E.ATTN_ERR_UNSUPPORTED
+    assert unfused(lib, idt=E.ATTN_F16) == E.ATTN_ERR_UNSUPPORTED
+    assert kvstore(lib, dt=3) == E.ATTN_ERR_UNSUPPORTED

@@ -17,7 +17,7 @@ def _bits(t):
     return t.view(torch.int16 if t.element_size() == 2 else torch.int32).cpu().numpy()
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
 @pytest.mark.parametrize("case", ["decode_like", "prefix_like"])
 def test_kv_store_bit_exact(dtype, case):
     log(f"kv_store {case} {dtype}")

@@ -208,6 +208,30 @@ def fp32_stress(L=256, d=64, seed=1001) -> Varlen:
     return Varlen(q, k, v, cu, cu.clone(), L, L, 1.0 / 8.0, True, "fp32_stress_L256_d64")
 
 
+def fp16_stress(L=300, hq=8, hkv=2, d=128, seed=1601) -> Varlen:
+    """The large-logit stress input for fp16 inputs (the overflow example of
+    the safe-softmax section, with fp16 named as the type that overflows).
+    Every query row is (16, 0, ..., 0) and the scale is 1/16, so the scaled
+    logit of key j is exactly K[j, 0] (the products are exact in fp32).
+    K[0:3, 0] = 700, 710, 705; K[j, 0] = 700 + delta_j for j >= 3 with
+    delta_j drawn from N(0, 5^2) and rounded to a 2^-1 grid, so every logit
+    is an exact fp16 value.  Other K columns are N(0, 1) (they meet zeros in
+    q).  V is N(0, 1).  Causal, one sequence, GQA heads sharing the K
+    column."""
+    g = _gen(seed)
+    q = torch.zeros(L, hq, d, dtype=torch.float32)
+    q[:, :, 0] = 16.0
+    k = torch.randn(L, hkv, d, generator=g, dtype=torch.float32)
+    delta = torch.round(torch.randn(L, generator=g, dtype=torch.float32) * 5.0 * 2.0) / 2.0
+    col = 700.0 + delta
+    col[0], col[1], col[2] = 700.0, 710.0, 705.0
+    k[:, :, 0] = col[:, None]
+    v = torch.randn(L, hkv, d, generator=g, dtype=torch.float32)
+    cu = _cumsum0([L])
+    return Varlen(q.to(torch.float16), k.to(torch.float16), v.to(torch.float16), cu, cu.clone(),
+                  L, L, 1.0 / 16.0, True, f"fp16_stress_L{L}")
+
+
 def varlen_prefill(n_seqs=16, lo=128, hi=4096, hq=32, hkv=8, d=128, seed=1002,
                    dtype=torch.bfloat16) -> Varlen:
     """Varlen causal prefill: n_seqs sequences with lengths uniform in
