@@ -48,7 +48,7 @@ KERNEL_SOURCES = {
     "decode": ["attention_sdpa_amd/csrc/decode.hip", "attention_sdpa_amd/csrc/device_common.h",
                "attention_sdpa_amd/csrc/launch.h"],
 }
-TRAFFIC_FILES = {"prefill": "profiles/prefill_bf16_varlen16_pmc.md",
+TRAFFIC_FILES = {"prefill": "profiles/prefill_mfma_varlen16_pmc.md",
                  "decode": "profiles/decode_paged_b64_pmc.md"}
 
 
@@ -221,10 +221,11 @@ def bench_unfused(args, torch, attn, workloads, fused_ms):
     lq = (vl.cu_seqlens_q[1:] - vl.cu_seqlens_q[:-1]).tolist()
     lk = (vl.cu_seqlens_k[1:] - vl.cu_seqlens_k[:-1]).tolist()
     pairs_all = float(sum(a * b for a, b in zip(lq, lk)))
-    # X written (fp32) and read back, A written (bf16) and read back, per
-    # (query, key) pair and query head: the round trips the fused kernel avoids
-    xa_bytes = pairs_all * 32 * (4 + 4 + 2 + 2)
     pairs = visible_pairs(vl.cu_seqlens_q.tolist(), vl.cu_seqlens_k.tolist(), True)
+    # the round trips the fused kernel avoids, per query head: X written for
+    # every (query, key) pair (fp32) and read back for the visible ones, A
+    # written (bf16) for every pair and read back
+    xa_bytes = 32 * (pairs_all * (4 + 2 + 2) + pairs * 4)
     flops = 4.0 * 128 * 32 * pairs
     del ws
     return {"workload": "the headline varlen causal prefill, unfused: X = s*QK^T (fp32) and "
@@ -362,7 +363,7 @@ def main():
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(pre["tflops_kernel"] / PEAK_BF16_TFLOPS, 4),
                          "traffic": recorded_traffic("prefill"),
-                         "kernel": "prefill_mfma_kernel<bf16>",
+                         "kernel": "prefill_mfma_kernel<bf16, true>",
                          "kernel_ms": round(pre["kernel_ms"], 4)},
         })
     if "decode" in res:
@@ -376,7 +377,7 @@ def main():
                              "peak": PEAK_HBM_GBS, "unit": "GB/s",
                              "frac": round(dec["gbs_kernel"] / PEAK_HBM_GBS, 4),
                              "traffic": recorded_traffic("decode"),
-                             "kernel": "decode_split_kernel<128> + decode_combine_kernel<128>",
+                             "kernel": "decode_split_kernel<bf16, 128> + decode_combine_kernel<bf16, 128>",
                              "kernel_ms": round(dec["kernel_ms"], 4)}}
         if "prefill" in res:
             line["decode"] = dobj
