@@ -137,6 +137,7 @@ ATTN_API int attn_prefill_varlen(const void *q, const void *k, const void *v, vo
     a.block_table = block_table;
     a.batch = batch;
     a.max_seqlen_q = max_seqlen_q;
+    a.max_seqlen_k = max_seqlen_k;
     a.total_q = total_q;
     a.total_k = paged ? 0 : total_k;
     a.hq = num_q_heads; a.hkv = num_kv_heads; a.d = head_dim;
@@ -190,6 +191,7 @@ ATTN_API int attn_prefill_padded(const void *q, const void *k, const void *v, vo
     a.block_table = nullptr;
     a.batch = batch;
     a.max_seqlen_q = max_seqlen_q;
+    a.max_seqlen_k = max_seqlen_k;
     a.total_q = total_q;
     a.total_k = total_k;
     a.hq = num_q_heads; a.hkv = num_kv_heads; a.d = head_dim;

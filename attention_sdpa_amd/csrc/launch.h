@@ -24,6 +24,7 @@ struct VarlenArgs {
     const int32_t *block_table;  // NULL: contiguous K/V
     int batch;
     int max_seqlen_q;
+    int max_seqlen_k;  // bound of the key counts (only orders the unit schedule)
     int64_t total_q;
     int64_t total_k;
     int hq;

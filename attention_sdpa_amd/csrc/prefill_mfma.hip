@@ -139,11 +139,12 @@ __device__ __forceinline__ void stage_barrier() {
 // ("strided" schedule), which is correct for any size but less balanced.
 
 constexpr int kMaxBatchListed = 1024;   // sequences
-constexpr int kMaxRowsListed = 4096;    // query blocks per sequence
+constexpr int kMaxRowsListed = 4096;    // query blocks per sequence; cost buckets
 constexpr int kMaxUnitsListed = 2048;   // units per workgroup
 
 struct Geo {
     int nqt;            // query-position blocks per sequence (upper bound)
+    int nct;            // listed schedule: cost buckets (64-key tile counts 0 .. nct-1)
     int hpw;            // query heads per wave column
     int head_chunks;    // group / hpw
     int pos_per_wg;     // query positions per unit
@@ -210,6 +211,54 @@ __device__ __forceinline__ void unit_bounds(const VarlenArgs &a, const Geo &geo,
     const int last = min(u.p0 + geo.pos_per_wg, u.Lq) - 1;
     u.kv_end = a.causal ? max(0, min(u.Lk, last + (u.Lk - u.Lq) + 1)) : u.Lk;
     u.n_tiles = (u.kv_end + kBN - 1) / kBN;
+}
+
+// Cost of the listed schedule's unit (query block qt of a sequence with Lq
+// queries and Lk keys, P query positions per unit): its number of 64-key
+// tiles, as unit_bounds counts them, with the per-sequence tile count
+// clamped to nct - 1 (the histogram's range).  Under the end-aligned causal
+// mask block qt < nq - 1 sees keys [0, P (qt + 1) + Lk - Lq), so its cost is
+// s (qt + 1) + e clamped to [0, Tk] with s = P / 64, e = ceil((Lk - Lq) / 64),
+// Tk = ceil(Lk / 64); the last block sees every key.
+__device__ __forceinline__ int ceil_div_signed(int a, int b) { return a >= 0 ? (a + b - 1) / b : -((-a) / b); }
+
+__device__ __forceinline__ int unit_cost(int causal, int Lq, int Lk, int qt, int P, int nct) {
+    const int nq = (Lq + P - 1) / P;
+    const int Tk = min((Lk + kBN - 1) / kBN, nct - 1);
+    if (!causal || qt == nq - 1) return Tk;
+    const int v = (P / kBN) * (qt + 1) + ceil_div_signed(Lk - Lq, kBN);
+    return v < 0 ? 0 : (v > Tk ? Tk : v);
+}
+
+// The query blocks of one sequence whose unit_cost is c: cnt of them,
+// starting at block first (they are contiguous).
+__device__ __forceinline__ void unit_cost_range(int causal, int Lq, int Lk, int c, int P, int nct, int &cnt,
+                                                int &first) {
+    cnt = 0;
+    first = 0;
+    const int nq = (Lq + P - 1) / P;
+    if (nq <= 0) return;
+    const int Tk = min((Lk + kBN - 1) / kBN, nct - 1);
+    if (!causal || Tk == 0) {
+        if (c == Tk) cnt = nq;
+        return;
+    }
+    const int s = P / kBN, e = ceil_div_signed(Lk - Lq, kBN);
+    if (c == Tk) {
+        int qT = ceil_div_signed(Tk - e, s) - 1;
+        qT = qT < 0 ? 0 : (qT > nq - 1 ? nq - 1 : qT);
+        cnt = nq - qT;
+        first = qT;
+    } else if (c == 0) {
+        int n0 = e <= 0 ? (-e) / s : 0;
+        cnt = n0 > nq - 1 ? nq - 1 : n0;
+    } else if (c > 0 && c < Tk && (c - e) % s == 0) {
+        const int qt = (c - e) / s - 1;
+        if (qt >= 0 && qt <= nq - 2) {
+            cnt = 1;
+            first = qt;
+        }
+    }
 }
 
 // Strided schedule: the first unit at or after slot counter k (with rows;
@@ -324,31 +373,38 @@ prefill_mfma_kernel(VarlenArgs a, Geo geo) {
     const bool paged = a.block_table != nullptr;
 
     // ---- listed schedule: this workgroup's units --------------------------
+    // Units are sorted by cost (their K/V tile count), heaviest first, and
+    // dealt to workgroups in a snake.  The cost of (sequence b, query block
+    // qt) is closed-form (see unit_cost); within one sequence the blocks of
+    // a given cost form a contiguous range (unit_cost_range), so the sort is
+    // a counting sort: a histogram over cost, two scans, and a closed-form
+    // lookup of each unit.  Row r of the histogram holds cost nct - 1 - r.
     int n_mine = 0;
     if constexpr (kListed) {
-        const int nqt = geo.nqt, P = geo.pos_per_wg;
+        const int nqt = geo.nqt, P = geo.pos_per_wg, nct = geo.nct;
         const int hcg = geo.head_chunks * a.hkv;
         for (int b = tid; b < a.batch; b += kThreads) {
             const SeqMeta m = seq_meta(a, b);
             sMeta[b] = make_int4(m.q0, m.Lq, m.k0, m.Lk);
         }
-        for (int r = tid; r < nqt; r += kThreads) sRows[r] = 0;
+        for (int r = tid; r < nct; r += kThreads) sRows[r] = 0;
         __syncthreads();
-        // sequence b has units in rows r >= nqt - nq_b
-        for (int b = tid; b < a.batch; b += kThreads) {
-            const int nq = min(nqt, (sMeta[b].y + P - 1) / P);
-            if (nq > 0) atomicAdd(&sRows[nqt - nq], 1);
+        // histogram of pair costs: pairs (qt, b) flattened, b fastest
+        for (int i = tid; i < nqt * a.batch; i += kThreads) {
+            const int qt = i / a.batch, b = i - qt * a.batch;
+            const int4 mm = sMeta[b];
+            if (qt * P < mm.y) atomicAdd(&sRows[nct - 1 - unit_cost(a.causal, mm.y, mm.w, qt, P, nct)], 1);
         }
         __syncthreads();
-        // two inclusive scans: sequences per row, then sequences in rows <= r
+        // one inclusive scan: pairs in rows <= r
         constexpr int kPer = kMaxRowsListed / kThreads;
-        for (int pass = 0; pass < 2; ++pass) {
+        {
             int v[kPer];
             int sum = 0;
 #pragma unroll
             for (int i = 0; i < kPer; ++i) {
                 const int r = tid * kPer + i;
-                sum += (r < nqt) ? sRows[r] : 0;
+                sum += (r < nct) ? sRows[r] : 0;
                 v[i] = sum;
             }
             int x = sum;
@@ -364,18 +420,20 @@ prefill_mfma_kernel(VarlenArgs a, Geo geo) {
 #pragma unroll
             for (int i = 0; i < kPer; ++i) {
                 const int r = tid * kPer + i;
-                if (r < nqt) sRows[r] = v[i] + excl;
+                if (r < nct) sRows[r] = v[i] + excl;
             }
             __syncthreads();
         }
         // units in rows < r: hcg * sRows[r - 1]
         const int grid = (int)gridDim.x, wg = (int)blockIdx.x;
-        const int u_total = hcg * sRows[nqt - 1];
+        const int u_total = hcg * sRows[nct - 1];
         const int rounds = u_total / grid, rem = u_total - rounds * grid;
         n_mine = rounds + ((((rounds & 1) ? grid - 1 - wg : wg) < rem) ? 1 : 0);
+        // the launch bounds the unit count so that the list fits; never write past it
+        n_mine = min(n_mine, kMaxUnitsListed);
         for (int k = w; k < n_mine; k += kWaves) {
             const int u = k * grid + ((k & 1) ? grid - 1 - wg : wg);
-            int lo = 0, hi = nqt - 1;
+            int lo = 0, hi = nct - 1;
             while (lo < hi) {
                 const int mid = (lo + hi + 1) >> 1;
                 if (hcg * __builtin_amdgcn_readfirstlane(sRows[mid - 1]) <= u) lo = mid;
@@ -383,28 +441,34 @@ prefill_mfma_kernel(VarlenArgs a, Geo geo) {
             }
             const int j = u - (lo ? hcg * __builtin_amdgcn_readfirstlane(sRows[lo - 1]) : 0);
             const int bi = j / hcg, rm = j - bi * hcg;
-            // the bi-th sequence (in index order) present in row lo
-            int seen = 0, bsel = 0;
+            const int c = nct - 1 - lo;
+            // the bi-th pair of cost c, in (b, qt) order
+            int seen = 0, bsel = 0, qsel = 0;
             for (int b0 = 0; b0 < a.batch; b0 += 64) {
                 const int b = b0 + lane;
-                bool ok = false;
+                int cnt = 0, first = 0;
                 if (b < a.batch) {
-                    const int nq = min(nqt, (sMeta[b].y + P - 1) / P);
-                    ok = nq > 0 && nqt - nq <= lo;
+                    const int4 mm = sMeta[b];
+                    unit_cost_range(a.causal, mm.y, mm.w, c, P, nct, cnt, first);
                 }
-                const uint64_t msk = __builtin_amdgcn_ballot_w64(ok);
-                const int c = __builtin_popcountll(msk);
-                if (bi < seen + c) {
-                    const int pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(msk >> 32),
-                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)msk, 0));
-                    const uint64_t hit = __builtin_amdgcn_ballot_w64(ok && pre == bi - seen);
-                    bsel = b0 + (int)__builtin_ctzll(hit);
+                int x = cnt;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const int y = __shfl_up(x, off, 64);
+                    if (lane >= off) x += y;
+                }
+                const int tot = __shfl(x, 63, 64);
+                if (bi < seen + tot) {
+                    const uint64_t hit = __builtin_amdgcn_ballot_w64(seen + x > bi);
+                    const int l = (int)__builtin_ctzll(hit);
+                    bsel = b0 + l;
+                    qsel = __shfl(first, l, 64) + (bi - seen - (__shfl(x, l, 64) - __shfl(cnt, l, 64)));
                     break;
                 }
-                seen += c;
+                seen += tot;
             }
-            const int qt = nqt - 1 - lo, g = rm % a.hkv, hc = rm / a.hkv;
-            if (lane == 0) sList[k] = make_int2(bsel, (qt << 16) | (hc << 8) | g);
+            const int g = rm % a.hkv, hc = rm / a.hkv;
+            if (lane == 0) sList[k] = make_int2(bsel, (qsel << 16) | (hc << 8) | g);
         }
         __syncthreads();
     }
@@ -839,6 +903,10 @@ hipError_t launch_prefill_typed(const VarlenArgs &a, hipStream_t stream) {
     geo.head_chunks = group / geo.hpw;
     geo.pos_per_wg = kRowsPerWave * (kWaves / geo.hpw);
     geo.nqt = (a.max_seqlen_q + geo.pos_per_wg - 1) / geo.pos_per_wg;
+    {
+        const int64_t nct = ((int64_t)a.max_seqlen_k + kBN - 1) / kBN + 1;
+        geo.nct = (int)(nct < kMaxRowsListed ? nct : kMaxRowsListed);
+    }
     auto lg2 = [](int x) { int l = 0; while ((1 << l) < x) ++l; return l; };
     geo.lg = lg2(a.hkv);
     geo.lhc = lg2(geo.head_chunks);

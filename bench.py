@@ -60,6 +60,9 @@ PREFILL_WORKLOADS = {
             "bf16 in/out, Q/K ~ N(0, 4), new K/V stored to a 256-token paged cache first",
     "noncausal": "varlen non-causal prefill: the 16-sequence batch of the headline workload "
                  "without the causal mask, bf16 in/out",
+    "prefix": "prefix-cache prefill: 32 sequences, new-token lengths U[1,512] attending to cached "
+              "prefixes U[1024,16384] plus themselves through a 256-token paged cache (new K/V "
+              "stored first), end-aligned causal mask, 32 Q / 8 KV heads, head_dim 128, bf16",
 }
 
 
@@ -128,7 +131,44 @@ def timed_loop(step, steps, warmup, torch, inner=None):
     return wall, kernel_ms
 
 
+def bench_prefix(args, torch, attn, workloads):
+    """Prefix-cache prefill: the new tokens' K/V are stored into the paged
+    cache, then the new queries attend to prefix + new keys through the
+    block table (end-aligned causal mask)."""
+    pp = workloads.prefix_prefill()
+    pg = pp.paged
+    q = pp.q.cuda()
+    kc, vc = pg.k_cache.cuda(), pg.v_cache.cuda()
+    kn, vn, slots = pg.k_new.cuda(), pg.v_new.cuda(), pg.slot_mapping.cuda()
+    cu_q, cu_k, bt = pp.cu_seqlens_q.cuda(), pg.cu_seqlens_k.cuda(), pg.block_table.cuda()
+    out = torch.empty_like(q)
+    Ev = torch.cuda.Event
+
+    def step(i):
+        attn.kv_store_slots(kn, vn, kc, vc, slots)
+        e0, e1 = Ev(enable_timing=True), Ev(enable_timing=True)
+        e0.record()
+        attn.attn_prefill_varlen(q, kc, vc, cu_q, cu_k, pp.max_seqlen_q, pp.max_seqlen_k,
+                                 pp.softmax_scale, True, block_table=bt, out=out)
+        e1.record()
+        return e0, e1
+
+    wall, kms = timed_loop(step, args.steps, args.warmup, torch)
+    pairs = visible_pairs(pp.cu_seqlens_q.tolist(), pg.cu_seqlens_k.tolist(), True)
+    flops = 4.0 * 128 * 32 * pairs
+    ms_step = wall * 1e3 / args.steps
+    k_ms = sum(kms) / len(kms)
+    total_k = int(pg.cu_seqlens_k[-1])
+    return dict(vl=None, flops=flops, ms_step=ms_step, kernel_ms=k_ms,
+                tflops_step=flops / (ms_step * 1e-3) / 1e12,
+                tflops_kernel=flops / (k_ms * 1e-3) / 1e12,
+                total_tokens=int(q.shape[0]),
+                bytes_alg=2.0 * (2 * q.numel() + 2 * total_k * 8 * 128))
+
+
 def bench_prefill(args, torch, attn, workloads):
+    if args.prefill_workload == "prefix":
+        return bench_prefix(args, torch, attn, workloads)
     if args.prefill_workload == "long":
         vl = workloads.long_prefill()
     elif args.prefill_workload == "noncausal":
@@ -292,9 +332,11 @@ def main():
     ap.add_argument("--only", choices=["all", "prefill", "decode", "unfused"], default="all")
     ap.add_argument("--skip-unfused", action="store_true",
                     help="omit the unfused three-kernel baseline (it needs ~52 GB of workspace)")
-    ap.add_argument("--prefill-workload", choices=["varlen", "long", "noncausal"], default="varlen",
+    ap.add_argument("--prefill-workload", choices=["varlen", "long", "noncausal", "prefix"],
+                    default="varlen",
                     help="prefill workload to time: the varlen 16-sequence batch (headline), the "
-                         "32768-token single sequence, or the varlen batch without the causal mask")
+                         "32768-token single sequence, the varlen batch without the causal mask, "
+                         "or the 32-sequence prefix-cache batch through the paged cache")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain elementwise copy of 1 GiB (read 1 GiB, write 1 GiB), "
                          "the reference for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -362,7 +404,9 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(pre["tflops_kernel"], 2),
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(pre["tflops_kernel"] / PEAK_BF16_TFLOPS, 4),
-                         "traffic": recorded_traffic("prefill"),
+                         # counters recorded for the headline workload only
+                         "traffic": recorded_traffic("prefill") if args.prefill_workload == "varlen"
+                         else None,
                          "kernel": "prefill_mfma_kernel<bf16, true>",
                          "kernel_ms": round(pre["kernel_ms"], 4)},
         })
@@ -387,7 +431,7 @@ def main():
                          "roofline": dobj["roofline"]})
     if "unfused" in res:
         line["unfused_baseline"] = res["unfused"]
-    if not args.skip_cpu and "prefill" in res:
+    if not args.skip_cpu and "prefill" in res and res["prefill"]["vl"] is not None:
         line["cpu_baseline"] = cpu_baseline_prefill(res["prefill"]["vl"], args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
