@@ -399,7 +399,7 @@ decode_split_kernel(DecodeArgs a) {
 template <typename T, int D>
 __global__ void __launch_bounds__(D)
 decode_combine_kernel(DecodeArgs a) {
-    constexpr int kBatchLoads = 4;  // partials read together
+    constexpr int kBatchLoads = 8;  // partials read together (a sequence spans few runs)
     const int bh = blockIdx.x;  // b * hq + h
     const int b = bh / a.hq;
     const int d = threadIdx.x;
