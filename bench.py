@@ -18,6 +18,9 @@ the paged cache (kv_store_slots), then attention.
   cached K and V byte read once per KV head; GB/s.
 * roofline: the prefill kernel alone, from events recorded around each of
   its launches inside the timed region, against bf16 dense MFMA peak.
+* other_prefill: the 32768-token sequence and the prefix-cache batch (32
+  sequences, 1-512 new tokens on 1K-16K cached ones, paged), a few timed
+  steps each, as TFLOP/s against the same peak.
 * unfused_baseline: the blog's standard three-step method (X and A stored in
   HBM between three kernels) on the same varlen workload, next to the fused
   kernel's time; skipped with --skip-unfused (it needs ~52 GB of workspace).
@@ -330,6 +333,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
     ap.add_argument("--only", choices=["all", "prefill", "decode", "unfused"], default="all")
+    ap.add_argument("--skip-other-prefill", action="store_true",
+                    help="omit the 32K-sequence and prefix-cache prefill timings of the default run")
     ap.add_argument("--skip-unfused", action="store_true",
                     help="omit the unfused three-kernel baseline (it needs ~52 GB of workspace)")
     ap.add_argument("--prefill-workload", choices=["varlen", "long", "noncausal", "prefix"],
@@ -381,6 +386,22 @@ def main():
               f"(fused kernel {fused_ms:.3f} ms), X/A traffic {unf['xa_gbs']:.0f} GB/s",
               file=sys.stderr, flush=True)
         res["unfused"] = unf
+    if args.only == "all" and args.prefill_workload == "varlen" and not args.skip_other_prefill:
+        # the other prefill configurations, a few timed steps each
+        import copy
+        other = {}
+        for w in ("long", "prefix"):
+            a2 = copy.copy(args)
+            a2.prefill_workload, a2.steps, a2.warmup = w, max(1, min(args.steps, 20)), max(1, min(args.warmup, 3))
+            r = bench_prefill(a2, torch, attn, workloads)
+            other[w] = {"workload": PREFILL_WORKLOADS[w], "steps": a2.steps,
+                        "algorithmic_flops": r["flops"], "kernel_ms": round(r["kernel_ms"], 4),
+                        "tflops": round(r["tflops_kernel"], 2),
+                        "frac": round(r["tflops_kernel"] / PEAK_BF16_TFLOPS, 4)}
+            print(f"[bench] {w} prefill kernel {r['kernel_ms']:.3f} ms, {r['tflops_kernel']:.1f} TFLOP/s",
+                  file=sys.stderr, flush=True)
+            del r
+        res["other_prefill"] = other
     if args.only in ("all", "decode"):
         dec = bench_decode(args, torch, attn, workloads)
         print(f"[bench] decode step {dec['ms_step']:.3f} ms, kernels {dec['kernel_ms']:.3f} ms, "
@@ -431,6 +452,8 @@ def main():
                          "roofline": dobj["roofline"]})
     if "unfused" in res:
         line["unfused_baseline"] = res["unfused"]
+    if "other_prefill" in res:
+        line["other_prefill"] = res["other_prefill"]
     if not args.skip_cpu and "prefill" in res and res["prefill"]["vl"] is not None:
         line["cpu_baseline"] = cpu_baseline_prefill(res["prefill"]["vl"], args.cpu_seconds)
     print(json.dumps(line), flush=True)
