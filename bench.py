@@ -450,6 +450,10 @@ def main():
             line.update({"value": dobj["value"], "unit": "GB/s", "ms_per_step": dobj["ms_per_step"],
                          "config": {"workload": dobj["workload"]},
                          "roofline": dobj["roofline"]})
+    props = torch.cuda.get_device_properties(0)
+    line["env"] = {"device": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
+                   "compute_units": props.multi_processor_count, "hip": torch.version.hip,
+                   "torch": torch.__version__}
     if "unfused" in res:
         line["unfused_baseline"] = res["unfused"]
     if "other_prefill" in res:
