@@ -138,7 +138,7 @@ def bench_prefix(args, torch, attn, workloads):
     """Prefix-cache prefill: the new tokens' K/V are stored into the paged
     cache, then the new queries attend to prefix + new keys through the
     block table (end-aligned causal mask)."""
-    pp = workloads.prefix_prefill()
+    pp = workloads.prefix_prefill(dtype=args.torch_dtype)
     pg = pp.paged
     q = pp.q.cuda()
     kc, vc = pg.k_cache.cuda(), pg.v_cache.cuda()
@@ -173,12 +173,12 @@ def bench_prefill(args, torch, attn, workloads):
     if args.prefill_workload == "prefix":
         return bench_prefix(args, torch, attn, workloads)
     if args.prefill_workload == "long":
-        vl = workloads.long_prefill()
+        vl = workloads.long_prefill(dtype=args.torch_dtype)
     elif args.prefill_workload == "noncausal":
-        vl = workloads.varlen_prefill()
+        vl = workloads.varlen_prefill(dtype=args.torch_dtype)
         vl.causal = False
     else:
-        vl = workloads.varlen_prefill()
+        vl = workloads.varlen_prefill(dtype=args.torch_dtype)
     cache = workloads.cache_for_varlen(vl, block_size=256, seed=5)
     q, k, v = vl.q.cuda(), vl.k.cuda(), vl.v.cuda()
     cu_q, cu_k = vl.cu_seqlens_q.cuda(), vl.cu_seqlens_k.cuda()
@@ -210,7 +210,7 @@ def bench_prefill(args, torch, attn, workloads):
 
 
 def bench_decode(args, torch, attn, workloads):
-    dc = workloads.paged_decode()
+    dc = workloads.paged_decode(dtype=args.torch_dtype)
     pg = dc.paged
     q = dc.q.cuda()
     kc, vc = pg.k_cache.cuda(), pg.v_cache.cuda()
@@ -333,6 +333,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
     ap.add_argument("--only", choices=["all", "prefill", "decode", "unfused"], default="all")
+    ap.add_argument("--dtype", choices=["bf16", "fp16"], default="bf16",
+                    help="16-bit input (and output) type of every workload")
     ap.add_argument("--skip-other-prefill", action="store_true",
                     help="omit the 32K-sequence and prefix-cache prefill timings of the default run")
     ap.add_argument("--skip-unfused", action="store_true",
@@ -355,6 +357,7 @@ def main():
     import torch
     import attention_sdpa_amd as attn
     import workloads
+    args.torch_dtype = torch.float16 if args.dtype == "fp16" else torch.bfloat16
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -379,7 +382,7 @@ def main():
               f"{pre['tflops_kernel']:.1f} TFLOP/s kernel", file=sys.stderr, flush=True)
         res["prefill"] = pre
     if args.only in ("all", "prefill", "unfused") and args.prefill_workload == "varlen" and \
-            not args.skip_unfused:
+            not args.skip_unfused and args.dtype == "bf16":
         fused_ms = res["prefill"]["kernel_ms"] if "prefill" in res else float("nan")
         unf = bench_unfused(args, torch, attn, workloads, fused_ms)
         print(f"[bench] unfused baseline {unf['kernel_ms']:.3f} ms "
@@ -394,7 +397,7 @@ def main():
             a2 = copy.copy(args)
             a2.prefill_workload, a2.steps, a2.warmup = w, max(1, min(args.steps, 20)), max(1, min(args.warmup, 3))
             r = bench_prefill(a2, torch, attn, workloads)
-            other[w] = {"workload": PREFILL_WORKLOADS[w], "steps": a2.steps,
+            other[w] = {"workload": PREFILL_WORKLOADS[w].replace("bf16", args.dtype), "steps": a2.steps,
                         "algorithmic_flops": r["flops"], "kernel_ms": round(r["kernel_ms"], 4),
                         "tflops": round(r["tflops_kernel"], 2),
                         "frac": round(r["tflops_kernel"] / PEAK_BF16_TFLOPS, 4)}
@@ -412,37 +415,37 @@ def main():
         "metric": "prefill attn TFLOP/s (% MFMA peak); paged decode KV GB/s (% HBM peak)",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic (seeded; no dataset or weights involved)",
+        "dtype": args.dtype, "data": "synthetic (seeded; no dataset or weights involved)",
     }
     if "prefill" in res:
         pre = res["prefill"]
         line.update({
             "value": round(pre["tflops_step"], 2), "unit": "TFLOP/s",
             "ms_per_step": round(pre["ms_step"], 4),
-            "config": {"workload": PREFILL_WORKLOADS[args.prefill_workload],
+            "config": {"workload": PREFILL_WORKLOADS[args.prefill_workload].replace("bf16", args.dtype),
                        "total_tokens": pre["total_tokens"], "algorithmic_flops": pre["flops"],
                        "step": "kv_store_slots + attn_prefill_varlen"},
             "roofline": {"bound": "mfma", "achieved": round(pre["tflops_kernel"], 2),
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(pre["tflops_kernel"] / PEAK_BF16_TFLOPS, 4),
                          # counters recorded for the headline workload only
-                         "traffic": recorded_traffic("prefill") if args.prefill_workload == "varlen"
-                         else None,
-                         "kernel": "prefill_mfma_kernel<bf16, true>",
+                         "traffic": recorded_traffic("prefill")
+                         if args.prefill_workload == "varlen" and args.dtype == "bf16" else None,
+                         "kernel": f"prefill_mfma_kernel<{args.dtype}, true>",
                          "kernel_ms": round(pre["kernel_ms"], 4)},
         })
     if "decode" in res:
         dec = res["decode"]
         dobj = {"workload": "paged decode: batch 64, contexts U[512,8192], block 256, permuted "
-                            "pool, 32 Q / 8 KV heads, head_dim 128, bf16, new token stored first",
+                            f"pool, 32 Q / 8 KV heads, head_dim 128, {args.dtype}, new token stored first",
                 "metric": "KV GB/s", "value": round(dec["gbs_step"], 1),
                 "ms_per_step": round(dec["ms_step"], 4),
                 "kv_bytes": dec["kv_bytes"],
                 "roofline": {"bound": "hbm", "achieved": round(dec["gbs_kernel"], 1),
                              "peak": PEAK_HBM_GBS, "unit": "GB/s",
                              "frac": round(dec["gbs_kernel"] / PEAK_HBM_GBS, 4),
-                             "traffic": recorded_traffic("decode"),
-                             "kernel": "decode_split_kernel<bf16, 128> + decode_combine_kernel<bf16, 128>",
+                             "traffic": recorded_traffic("decode") if args.dtype == "bf16" else None,
+                             "kernel": f"decode_split_kernel<{args.dtype}, 128> + decode_combine_kernel<{args.dtype}, 128>",
                              "kernel_ms": round(dec["kernel_ms"], 4)}}
         if "prefill" in res:
             line["decode"] = dobj
