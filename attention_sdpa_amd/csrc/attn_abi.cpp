@@ -103,7 +103,9 @@ ATTN_API int attn_prefill_varlen(const void *q, const void *k, const void *v, vo
                                  const int32_t *block_table, int max_blocks_per_seq,
                                  int num_blocks, int block_size,
                                  int in_dtype, int out_dtype, void *stream) {
-    if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_k) return ATTN_ERR_NULL;
+    // K and V may be NULL only when there is no key to read
+    const bool no_keys = block_table == nullptr && total_k == 0;
+    if (!q || !o || !cu_seqlens_q || !cu_seqlens_k || (!no_keys && (!k || !v))) return ATTN_ERR_NULL;
     if (batch <= 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 ||
         num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0)
         return ATTN_ERR_SHAPE;
@@ -163,7 +165,8 @@ ATTN_API int attn_prefill_padded(const void *q, const void *k, const void *v, vo
                                  int num_q_heads, int num_kv_heads, int head_dim,
                                  float softmax_scale, int causal, int in_dtype, int out_dtype,
                                  void *stream) {
-    if (!q || !k || !v || !o || !seqlens_q || !seqlens_k) return ATTN_ERR_NULL;
+    // K and V may be NULL only when there is no key to read
+    if (!q || !o || !seqlens_q || !seqlens_k || (max_seqlen_k != 0 && (!k || !v))) return ATTN_ERR_NULL;
     if (batch <= 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
         head_dim <= 0)
         return ATTN_ERR_SHAPE;

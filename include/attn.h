@@ -123,7 +123,8 @@ int kv_store_slots(const void *k, const void *v, void *k_cache, void *v_cache,
  * (fp32 throughout; out_dtype ATTN_F32 or ATTN_BF16); conversions round to
  * nearest even;
  * num_q_heads a multiple of num_kv_heads; block_size a multiple of 64 when
- * paged.  Pointers must be 16-byte aligned.
+ * paged.  Pointers must be 16-byte aligned; k and v may be NULL when
+ * block_table is NULL and total_k is 0 (no key anywhere; every row is 0).
  */
 int attn_prefill_varlen(const void *q, const void *k, const void *v, void *o,
                         const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
@@ -153,8 +154,9 @@ int attn_prefill_varlen(const void *q, const void *k, const void *v, void *o,
  *   seqlens_k      [batch] int32 device arrays
  *
  * Supported: as attn_prefill_varlen with contiguous K/V; batch *
- * max_seqlen_q and batch * max_seqlen_k below 2^31.  Errors as
- * attn_prefill_varlen.
+ * max_seqlen_q and batch * max_seqlen_k below 2^31.  k and v may be NULL
+ * when max_seqlen_k is 0 (no sequence has a key; every valid row is 0).
+ * Errors as attn_prefill_varlen.
  */
 int attn_prefill_padded(const void *q, const void *k, const void *v, void *o,
                         const int32_t *seqlens_q, const int32_t *seqlens_k,

@@ -228,3 +228,13 @@ def test_fp16_validation(lib):
     assert padded(lib, idt=E.ATTN_F16, odt=E.ATTN_BF16) == E.ATTN_ERR_UNSUPPORTED
     assert unfused(lib, idt=E.ATTN_F16) == E.ATTN_ERR_UNSUPPORTED
     assert kvstore(lib, dt=3) == E.ATTN_ERR_UNSUPPORTED
+
+
+def test_null_kv_only_without_keys(lib):
+    """K/V may be NULL only when no key exists (the kernels never read them
+    then); otherwise a null K or V is ATTN_ERR_NULL."""
+    E = attn
+    assert prefill(lib, k=None) == E.ATTN_ERR_NULL
+    assert prefill(lib, v=None, total_k=0, bt=P2, mbs=4, nb=4, bs=64) == E.ATTN_ERR_NULL   # paged: never
+    assert padded(lib, k=None) == E.ATTN_ERR_NULL
+    assert padded(lib, k=None, v=None, maxq=0, maxk=0) == E.ATTN_OK     # nothing to do at all

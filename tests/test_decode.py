@@ -159,3 +159,12 @@ def test_decode_reused_workspace():
         torch.cuda.synchronize()
         log(f"case decode reused workspace call {i}")
         check_bf16(np32(got), oracle_decode(dc), f"decode reused workspace call {i}")
+
+
+def test_decode_all_contexts_empty():
+    """Every context length 0: the key stream has no item at all, no run is
+    used, and every output row is 0."""
+    dc = make_decode([0, 0, 0], seed=31, mbs=2)
+    log("case decode all contexts empty")
+    got = run_decode(dc)
+    assert np.all(np32(got) == 0)

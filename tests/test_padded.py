@@ -98,3 +98,19 @@ def test_padded_equals_varlen_bits():
     torch.cuda.synchronize()
     log("case padded == varlen bits")
     assert np.array_equal(got, np32(packed))
+
+
+def test_padded_no_keys_at_all():
+    """max_seqlen_k = 0: no sequence has a key, so every valid output row is
+    0 (and padded rows stay untouched)."""
+    q = torch.randn(2, 4, 8, 128).to(torch.bfloat16)
+    k = torch.empty(2, 0, 2, 128, dtype=torch.bfloat16)
+    lq = torch.tensor([3, 4], dtype=torch.int32)
+    lk = torch.tensor([0, 0], dtype=torch.int32)
+    out = torch.full((2, 4, 8, 128), SENTINEL, dtype=torch.float32, device="cuda")
+    log("case padded no keys")
+    attn.attn_prefill_padded(dev(q), dev(k), dev(k), dev(lq), dev(lk), 0.1, True, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu()
+    assert torch.all(got[0, :3] == 0) and torch.all(got[1, :4] == 0)
+    assert torch.all(got[0, 3:] == SENTINEL)

@@ -76,3 +76,14 @@ def test_unfused_reused_workspace():
     log("case unfused reused workspace")
     for vl in (a, b, a):
         check_bf16(np32(run_unfused(vl, workspace=ws)), oracle_varlen(vl), "unfused reuse")
+
+
+def test_unfused_sequence_without_keys():
+    """A sequence with queries but no keys gives zero rows; its neighbours
+    are unaffected."""
+    vl = workloads.varlen([4, 6, 3], [5, 0, 3], 8, 2, 128, torch.bfloat16, seed=10)
+    log("case unfused sequence without keys")
+    for causal in (True, False):
+        got = np32(run_unfused(vl, causal=causal))
+        assert np.all(got[4:10] == 0)
+        check_bf16(got, oracle_varlen(vl, causal=causal), f"unfused no-key sequence causal={causal}")
