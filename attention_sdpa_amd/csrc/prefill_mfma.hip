@@ -50,7 +50,7 @@
 //   counts that follow are exact.
 // * Causal: tiles past the last visible key are never loaded; only tiles
 //   that cross the diagonal (or the sequence end) are masked.  Work units are
-//   dealt heavy-first (latest query blocks first) and the KV head is the
+//   dealt heaviest first (by K/V tile count) and the KV head is the
 //   fastest-varying index, so that each XCD keeps reusing few heads' K/V in
 //   its L2.
 // * Exponentials in base 2 with c = s*log2(e): p = 2^(fma(x, c, -r*c)) for a
@@ -127,14 +127,14 @@ __device__ __forceinline__ void stage_barrier() {
 // A unit is (sequence b, query block qt, head chunk hc, KV head g): the
 // pos_per_wg query positions from qt * pos_per_wg of the hpw query heads
 // (chunk hc of g's GQA group) that read KV head g.  Its cost is its number
-// of K/V tiles, which under the causal mask grows with qt.  Units are put in
-// rows r = 0, 1, ... with qt = nqt-1-r, so heavier rows come first; row r
-// holds, for every sequence with more than qt query blocks (in sequence
-// order), its head_chunks * hkv units, g fastest.  Unit u of that order
-// goes to workgroup snake(u): round u / grid, position u % grid, reversed
-// in odd rounds -- the greedy assignment for rounds of equal-cost units.
-// Every workgroup derives its own list from cu_seqlens_q at start ("listed"
-// schedule).  Where the sizes exceed the tables below, workgroup i instead
+// of K/V tiles (under the causal mask it grows with qt, and with the
+// sequence's cached prefix).  Units are sorted by cost, heaviest first: row
+// r holds the units of cost nct-1-r, (sequence, query block) pairs in
+// (b, qt) order, each with its head_chunks * hkv units, g fastest.  Unit u
+// of that order goes to workgroup snake(u): round u / grid, position
+// u % grid, reversed in odd rounds -- the greedy assignment for rounds of
+// near-equal-cost units.  Every workgroup derives its own list from
+// cu_seqlens_q/k at start ("listed" schedule).  Where the sizes exceed the tables below, workgroup i instead
 // takes slots i, i + grid, ... of the padded (qt, b, hc, g) slot grid
 // ("strided" schedule), which is correct for any size but less balanced.
 
@@ -854,10 +854,12 @@ prefill_mfma_kernel(VarlenArgs a, Geo geo) {
             if (grpA) even_barrier();
             else odd_barrier();
             __builtin_amdgcn_s_setprio(1);
+            // this step's K/V batch first: the stage it refills was last read
+            // in the previous step, before the barrier just passed
+            issue();
             // every wave runs every step: past its last visible tile its P is
             // zero (adding exactly 0)
             mma(st1, st, std::true_type{});
-            issue();
             __builtin_amdgcn_s_setprio(0);
             if (grpA) odd_barrier();
             else even_barrier();
