@@ -31,7 +31,7 @@
 //   one query per lane, so any rescale is lane-local.
 // * Two groups of four wavefronts (one wave of each group per SIMD) run a
 //   ping-pong: while one group runs its matrix phase (the next tile's S^T and
-//   this tile's P V, MFMA after MFMA with LDS operand reads four steps
+//   this tile's P V, MFMA after MFMA with LDS operand reads two steps
 //   ahead), the other computes a softmax on the vector ALUs; a workgroup
 //   barrier separates the half-steps.
 // * K/V tiles reach LDS by direct global->LDS loads (global_load_lds_dwordx4,
@@ -733,7 +733,7 @@ prefill_mfma_kernel(VarlenArgs a, Geo geo) {
         // the operands of step i + kAhead are read from LDS during step i.
         auto mma = [&](int ks, int vs, auto with_qk) ATTN_INLINE {
             constexpr bool kQK = decltype(with_qk)::value;
-            constexpr int kAhead = 4;
+            constexpr int kAhead = 2;   // measured best of 1..5
             const bf16 *Kt = &sK[0][0] + ks * kTileElems;
             const bf16 *Vt = &sV[0][0] + vs * kTileElems;
             T8 kbuf[16], vbuf[16];
