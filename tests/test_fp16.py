@@ -117,3 +117,33 @@ def test_fp16_padded():
     got = np.concatenate([np32(out[b, :lq[b]]) for b in range(3)])
     log("case fp16 padded")
     check_f16(got, oracle_varlen(vl), "fp16 padded")
+
+
+def test_full_fp16_varlen_prefill_16_seqs():
+    """The headline varlen workload (16 sequences, U[128, 4096]) with fp16
+    inputs, in the launch configuration the benchmark times, on sampled rows
+    (first, middle and last token of every sequence for three heads, plus
+    random rows)."""
+    from tests.helpers import sample_rows
+    vl = workloads.varlen_prefill(dtype=F16)
+    log(f"case fp16 {vl.name}")
+    got = run_varlen(vl)
+    rows = sample_rows(vl.cu_seqlens_q, 32, 600, seed=3)
+    check_f16(np32(got).reshape(-1, 128)[rows], oracle_varlen(vl, rows=rows), "fp16 varlen 16 seqs (sampled)")
+    assert torch.isfinite(got).all().item()
+
+
+def test_full_fp16_paged_decode_64():
+    """The decode workload (batch 64, contexts U[512, 8192], block 256,
+    permuted pool) with fp16 inputs, every output row."""
+    dc = workloads.paged_decode(dtype=F16)
+    pg = dc.paged
+    kc, vc = dev(pg.k_cache), dev(pg.v_cache)
+    attn.kv_store_slots(dev(pg.k_new), dev(pg.v_new), kc, vc, dev(pg.slot_mapping))
+    got = attn.attn_decode_paged(dev(dc.q), kc, vc, dev(pg.seqlens_k), dev(pg.block_table),
+                                 dc.softmax_scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    log("case fp16 decode 64")
+    ref = oracle.attn_decode(np32(dc.q), np32(pg.k_logical), np32(pg.v_logical),
+                             pg.cu_seqlens_k.numpy(), dc.softmax_scale)
+    check_f16(np32(got), ref, "fp16 decode 64 (all rows)")
