@@ -40,9 +40,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     global _lib
     if _lib is not None and path is None:
         return _lib
-    # ATTN_LIBRARY names an alternative build (A/B measurements); unset in
-    # normal use, where the in-tree libattn.so is loaded
-    p = path or os.environ.get("ATTN_LIBRARY") or LIB_PATH
+    p = path or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(f"{p} is missing: build it with `python -m attention_sdpa_amd.build` "
                            "(there is no fallback implementation)")
@@ -110,6 +108,33 @@ def _i32(t: Optional[torch.Tensor]):
     return _ptr(t)
 
 
+def _same_device(what: str, ref: torch.Tensor, *ts: Optional[torch.Tensor]):
+    for t in ts:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{what}: every tensor must be on {ref.device}, got {t.device}")
+
+
+def _need(cond: bool, what: str, msg: str):
+    if not cond:
+        raise ValueError(f"{what}: {msg}")
+
+
+def _index(t: torch.Tensor, n: int, what: str, name: str):
+    """A 1-D-like int32 index tensor with exactly n entries."""
+    if t.dtype != torch.int32:
+        raise TypeError(f"{what}: {name} must be int32")
+    _need(t.numel() == n, what, f"{name} has {t.numel()} entries, expected {n}")
+
+
+def _kv_pair(k: torch.Tensor, v: torch.Tensor, q: torch.Tensor, what: str):
+    """K and V agree with each other and with Q in dtype and head_dim."""
+    _need(k.dtype == v.dtype == q.dtype, what,
+          f"q, k and v must share a dtype (got {q.dtype}, {k.dtype}, {v.dtype})")
+    _need(k.shape == v.shape, what, f"k {tuple(k.shape)} and v {tuple(v.shape)} differ in shape")
+    _need(k.shape[-1] == q.shape[-1], what,
+          f"head_dim of k ({k.shape[-1]}) differs from q ({q.shape[-1]})")
+
+
 def _stream(stream=None):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -122,8 +147,11 @@ def kv_store_slots(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor, v_ca
     nb, bs = k_cache.shape[0], k_cache.shape[1]
     if k_cache.shape != v_cache.shape or k.shape != v.shape or tuple(k_cache.shape[2:]) != (hkv, d):
         raise ValueError("shape mismatch")
-    if slot_mapping.numel() != T or k.dtype != k_cache.dtype:
+    if slot_mapping.numel() != T or k.dtype != k_cache.dtype or v.dtype != k.dtype or v_cache.dtype != k.dtype:
         raise ValueError("slot_mapping/dtype mismatch")
+    if slot_mapping.dtype != torch.int32:
+        raise TypeError("kv_store_slots: slot_mapping must be int32")
+    _same_device("kv_store_slots", k, v, k_cache, v_cache, slot_mapping)
     lib = load_library()
     _check("kv_store_slots", lib.kv_store_slots(
         _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _i32(slot_mapping), T, hkv, d, nb, bs,
@@ -137,17 +165,31 @@ def attn_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                         out: Optional[torch.Tensor] = None, out_dtype=None, stream=None) -> torch.Tensor:
     """Varlen prefill.  block_table=None: k/v packed [total_k, Hkv, d];
     otherwise k/v are the paged caches [num_blocks, block_size, Hkv, d]."""
+    what = "attn_prefill_varlen"
+    _need(q.dim() == 3, what, f"q must be [total_q, Hq, d], got {tuple(q.shape)}")
     total_q, hq, d = q.shape
-    if out is None:
-        out = torch.empty((total_q, hq, d), dtype=out_dtype or q.dtype, device=q.device)
+    _kv_pair(k, v, q, what)
+    batch = cu_seqlens_q.numel() - 1
+    _need(batch >= 1, what, "cu_seqlens_q needs at least 2 entries")
+    _index(cu_seqlens_q, batch + 1, what, "cu_seqlens_q")
+    _index(cu_seqlens_k, batch + 1, what, "cu_seqlens_k")
     if block_table is None:
+        _need(k.dim() == 3, what, f"k must be [total_k, Hkv, d], got {tuple(k.shape)}")
         total_k, hkv = k.shape[0], k.shape[1]
         mbs = nb = bs = 0
     else:
+        _need(k.dim() == 4, what, f"paged k must be [num_blocks, block_size, Hkv, d], got {tuple(k.shape)}")
+        _need(block_table.dim() == 2 and block_table.shape[0] >= batch, what,
+              f"block_table must be [>= {batch}, max_blocks_per_seq], got {tuple(block_table.shape)}")
+        if block_table.dtype != torch.int32:
+            raise TypeError(f"{what}: block_table must be int32")
         total_k = 0
         nb, bs, hkv = k.shape[0], k.shape[1], k.shape[2]
         mbs = block_table.shape[1]
-    batch = cu_seqlens_q.numel() - 1
+    if out is None:
+        out = torch.empty((total_q, hq, d), dtype=out_dtype or q.dtype, device=q.device)
+    _need(tuple(out.shape) == (total_q, hq, d), what, f"out must be {(total_q, hq, d)}, got {tuple(out.shape)}")
+    _same_device(what, q, k, v, out, cu_seqlens_q, cu_seqlens_k, block_table)
     lib = load_library()
     _check("attn_prefill_varlen", lib.attn_prefill_varlen(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _i32(cu_seqlens_q), _i32(cu_seqlens_k), batch,
@@ -167,14 +209,25 @@ def attn_decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       split_tokens: int = 0, workspace: Optional[torch.Tensor] = None,
                       out: Optional[torch.Tensor] = None, out_dtype=None, stream=None) -> torch.Tensor:
     """Single-token decode; q [B, Hq, d], caches [num_blocks, block_size, Hkv, d]."""
+    what = "attn_decode_paged"
+    _need(q.dim() == 3, what, f"q must be [batch, Hq, d], got {tuple(q.shape)}")
     B, hq, d = q.shape
+    _kv_pair(k_cache, v_cache, q, what)
+    _need(k_cache.dim() == 4, what, f"caches must be [num_blocks, block_size, Hkv, d], got {tuple(k_cache.shape)}")
     nb, bs, hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    _index(cache_seqlens, B, what, "cache_seqlens")
+    _need(block_table.dim() == 2 and block_table.shape[0] >= B, what,
+          f"block_table must be [>= {B}, max_blocks_per_seq], got {tuple(block_table.shape)}")
+    if block_table.dtype != torch.int32:
+        raise TypeError(f"{what}: block_table must be int32")
     mbs = block_table.shape[1]
     if out is None:
         out = torch.empty((B, hq, d), dtype=out_dtype or q.dtype, device=q.device)
+    _need(tuple(out.shape) == (B, hq, d), what, f"out must be {(B, hq, d)}, got {tuple(out.shape)}")
     need = attn_decode_workspace_bytes(B, hq, hkv, d, mbs, bs, split_tokens)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _same_device(what, q, k_cache, v_cache, out, cache_seqlens, block_table, workspace)
     lib = load_library()
     _check("attn_decode_paged", lib.attn_decode_paged(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _i32(cache_seqlens), _i32(block_table),
@@ -194,14 +247,23 @@ def attn_prefill_unfused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                          out: Optional[torch.Tensor] = None, out_dtype=None, stream=None) -> torch.Tensor:
     """The unfused three-kernel baseline (X and A through HBM); arguments as
     attn_prefill_varlen with contiguous K/V."""
+    what = "attn_prefill_unfused"
+    _need(q.dim() == 3, what, f"q must be [total_q, Hq, d], got {tuple(q.shape)}")
     total_q, hq, d = q.shape
+    _kv_pair(k, v, q, what)
+    _need(k.dim() == 3, what, f"k must be [total_k, Hkv, d], got {tuple(k.shape)}")
     total_k, hkv = k.shape[0], k.shape[1]
     B = cu_seqlens_q.numel() - 1
+    _need(B >= 1, what, "cu_seqlens_q needs at least 2 entries")
+    _index(cu_seqlens_q, B + 1, what, "cu_seqlens_q")
+    _index(cu_seqlens_k, B + 1, what, "cu_seqlens_k")
     if out is None:
         out = torch.empty((total_q, hq, d), dtype=out_dtype or q.dtype, device=q.device)
+    _need(tuple(out.shape) == (total_q, hq, d), what, f"out must be {(total_q, hq, d)}, got {tuple(out.shape)}")
     need = attn_unfused_workspace_bytes(B, hq, max_seqlen_q, max_seqlen_k)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _same_device(what, q, k, v, out, cu_seqlens_q, cu_seqlens_k, workspace)
     lib = load_library()
     _check("attn_prefill_unfused", lib.attn_prefill_unfused(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _i32(cu_seqlens_q), _i32(cu_seqlens_k), B,
@@ -217,10 +279,18 @@ def attn_prefill_padded(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seqle
     """Prefill on a padded batch: q [B, Lq_max, Hq, d], k/v [B, Lk_max, Hkv, d],
     seqlens_q/seqlens_k [B] int32.  Output rows at or past seqlens_q[b] are
     left as they are in `out` (zeros when `out` is omitted)."""
+    what = "attn_prefill_padded"
+    _need(q.dim() == 4, what, f"q must be [B, Lq_max, Hq, d], got {tuple(q.shape)}")
     B, mq, hq, d = q.shape
+    _kv_pair(k, v, q, what)
+    _need(k.dim() == 4 and k.shape[0] == B, what, f"k must be [{B}, Lk_max, Hkv, d], got {tuple(k.shape)}")
     mk, hkv = k.shape[1], k.shape[2]
+    _index(seqlens_q, B, what, "seqlens_q")
+    _index(seqlens_k, B, what, "seqlens_k")
     if out is None:
         out = torch.zeros((B, mq, hq, d), dtype=out_dtype or q.dtype, device=q.device)
+    _need(tuple(out.shape) == (B, mq, hq, d), what, f"out must be {(B, mq, hq, d)}, got {tuple(out.shape)}")
+    _same_device(what, q, k, v, out, seqlens_q, seqlens_k)
     lib = load_library()
     _check("attn_prefill_padded", lib.attn_prefill_padded(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _i32(seqlens_q), _i32(seqlens_k), B, mq, mk, hq, hkv, d,

@@ -6,6 +6,7 @@
 // here allocates, synchronises or keeps state between calls.
 #include <hip/hip_runtime.h>
 
+#include <cfloat>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
@@ -24,6 +25,13 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int dtype_size(int dt) { return dt == ATTN_F32 ? 4 : ((dt == ATTN_BF16 || dt == ATTN_F16) ? 2 : 0); }
 
 bool is16(int dt) { return dt == ATTN_BF16 || dt == ATTN_F16; }
+
+// softmax_scale must be finite and positive, and large enough that s * log2(e)
+// is a normal float: the kernels form masked weights as 2^(-inf * c - m), which
+// is 0 only for c > 0 (c = 0 would give NaN, c < 0 would turn the mask around).
+bool scale_ok(float s) {
+    return std::isfinite(s) && (double)s * 1.4426950408889634 >= (double)FLT_MIN;
+}
 
 int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
@@ -110,7 +118,7 @@ ATTN_API int attn_prefill_varlen(const void *q, const void *k, const void *v, vo
         num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0)
         return ATTN_ERR_SHAPE;
     if (num_q_heads % num_kv_heads != 0) return ATTN_ERR_SHAPE;
-    if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return ATTN_ERR_SHAPE;
+    if (!scale_ok(softmax_scale)) return ATTN_ERR_SHAPE;
     const bool paged = block_table != nullptr;
     if (paged) {
         if (max_blocks_per_seq <= 0 || num_blocks <= 0 || block_size <= 0) return ATTN_ERR_SHAPE;
@@ -171,7 +179,7 @@ ATTN_API int attn_prefill_padded(const void *q, const void *k, const void *v, vo
         head_dim <= 0)
         return ATTN_ERR_SHAPE;
     if (num_q_heads % num_kv_heads != 0) return ATTN_ERR_SHAPE;
-    if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return ATTN_ERR_SHAPE;
+    if (!scale_ok(softmax_scale)) return ATTN_ERR_SHAPE;
     if (is16(in_dtype)) {
         if (head_dim != 128) return ATTN_ERR_UNSUPPORTED;
         if (out_dtype != ATTN_F32 && out_dtype != in_dtype) return ATTN_ERR_UNSUPPORTED;
@@ -224,19 +232,21 @@ ATTN_API size_t attn_decode_workspace_bytes(int batch, int num_q_heads, int num_
     return L.total;
 }
 
-ATTN_API int attn_decode_paged(const void *q, const void *k_cache, const void *v_cache,
-                               void *o, const int32_t *cache_seqlens,
-                               const int32_t *block_table, int batch, int num_q_heads,
-                               int num_kv_heads, int head_dim, int max_blocks_per_seq,
-                               int num_blocks, int block_size, float softmax_scale,
-                               int split_tokens, int in_dtype, int out_dtype,
-                               void *workspace, size_t workspace_bytes, void *stream) {
+namespace {
+
+// Validation and argument set-up shared by the two decode entry points; the
+// three workspace pointers are left for the caller to fill from L.
+int decode_prepare(const void *q, const void *k_cache, const void *v_cache, void *o,
+                   const int32_t *cache_seqlens, const int32_t *block_table, int batch,
+                   int num_q_heads, int num_kv_heads, int head_dim, int max_blocks_per_seq,
+                   int num_blocks, int block_size, float softmax_scale, int split_tokens,
+                   int in_dtype, int out_dtype, attn::DecodeArgs *a, DecodeLayout *L) {
     if (!q || !k_cache || !v_cache || !o || !cache_seqlens || !block_table) return ATTN_ERR_NULL;
     if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
         max_blocks_per_seq <= 0 || num_blocks <= 0 || block_size <= 0)
         return ATTN_ERR_SHAPE;
     if (num_q_heads % num_kv_heads != 0) return ATTN_ERR_SHAPE;
-    if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return ATTN_ERR_SHAPE;
+    if (!scale_ok(softmax_scale)) return ATTN_ERR_SHAPE;
     if (!is16(in_dtype) || head_dim != 128) return ATTN_ERR_UNSUPPORTED;
     if (out_dtype != ATTN_F32 && out_dtype != in_dtype) return ATTN_ERR_UNSUPPORTED;
     if (num_q_heads / num_kv_heads > 16) return ATTN_ERR_UNSUPPORTED;
@@ -244,33 +254,53 @@ ATTN_API int attn_decode_paged(const void *q, const void *k_cache, const void *v
     if (split_tokens < 0 || split_tokens % 32 != 0) return ATTN_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
         return ATTN_ERR_UNSUPPORTED;
-    DecodeLayout L;
     if (!decode_layout(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size,
-                       split_tokens, &L))
+                       split_tokens, L))
         return ATTN_ERR_SHAPE;
     if ((int64_t)max_blocks_per_seq * block_size > 0x7fffffffLL) return ATTN_ERR_SHAPE;
     if ((int64_t)batch * num_q_heads * head_dim > 0x7fffffffLL) return ATTN_ERR_SHAPE;
-    if (!workspace || workspace_bytes < L.total) return ATTN_ERR_WORKSPACE;
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_ERR_WORKSPACE;
+    a->q = q; a->k_cache = k_cache; a->v_cache = v_cache; a->o = o;
+    a->cache_seqlens = cache_seqlens; a->block_table = block_table;
+    a->batch = batch; a->hq = num_q_heads; a->hkv = num_kv_heads; a->d = head_dim;
+    a->max_blocks_per_seq = max_blocks_per_seq; a->num_blocks = num_blocks; a->block_size = block_size;
+    a->scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+    a->split_tokens = L->split;
+    a->out_f32 = out_dtype == ATTN_F32;
+    a->in_f16 = in_dtype == ATTN_F16;
+    return ATTN_OK;
+}
 
-    attn::DecodeArgs a;
-    a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.o = o;
-    a.cache_seqlens = cache_seqlens; a.block_table = block_table;
-    a.batch = batch; a.hq = num_q_heads; a.hkv = num_kv_heads; a.d = head_dim;
-    a.max_blocks_per_seq = max_blocks_per_seq; a.num_blocks = num_blocks; a.block_size = block_size;
-    a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
-    a.split_tokens = L.split;
+// Runs on the current device, then the launch on the workspace at ws.
+int decode_launch(attn::DecodeArgs *a, const DecodeLayout &L, void *ws, void *stream) {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return ATTN_ERR_HIP;
-    a.n_runs = attn::decode_runs(num_kv_heads, cus);
-    a.ws_o = reinterpret_cast<float *>(workspace);
-    a.ws_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + L.ml_off);
-    a.ws_runs = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(workspace) + L.runs_off);
-    a.out_f32 = out_dtype == ATTN_F32;
-    a.in_f16 = in_dtype == ATTN_F16;
-    return hip_status(attn::launch_decode(a, (hipStream_t)stream));
+    a->n_runs = attn::decode_runs(a->hkv, cus);
+    a->ws_o = reinterpret_cast<float *>(ws);
+    a->ws_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + L.ml_off);
+    a->ws_runs = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(ws) + L.runs_off);
+    return hip_status(attn::launch_decode(*a, (hipStream_t)stream));
+}
+
+}  // namespace
+
+ATTN_API int attn_decode_paged(const void *q, const void *k_cache, const void *v_cache,
+                               void *o, const int32_t *cache_seqlens,
+                               const int32_t *block_table, int batch, int num_q_heads,
+                               int num_kv_heads, int head_dim, int max_blocks_per_seq,
+                               int num_blocks, int block_size, float softmax_scale,
+                               int split_tokens, int in_dtype, int out_dtype,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+    attn::DecodeArgs a;
+    DecodeLayout L;
+    const int st = decode_prepare(q, k_cache, v_cache, o, cache_seqlens, block_table, batch, num_q_heads,
+                                  num_kv_heads, head_dim, max_blocks_per_seq, num_blocks, block_size,
+                                  softmax_scale, split_tokens, in_dtype, out_dtype, &a, &L);
+    if (st != ATTN_OK) return st;
+    if (!workspace || workspace_bytes < L.total) return ATTN_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_ERR_WORKSPACE;
+    return decode_launch(&a, L, workspace, stream);
 }
 
 namespace {
@@ -311,7 +341,7 @@ ATTN_API int attn_prefill_unfused(const void *q, const void *k, const void *v, v
         max_seqlen_k < 0 || total_q < 0 || total_k < 0)
         return ATTN_ERR_SHAPE;
     if (num_q_heads % num_kv_heads != 0) return ATTN_ERR_SHAPE;
-    if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return ATTN_ERR_SHAPE;
+    if (!scale_ok(softmax_scale)) return ATTN_ERR_SHAPE;
     if (in_dtype != ATTN_BF16 || head_dim != 128) return ATTN_ERR_UNSUPPORTED;
     if (out_dtype != ATTN_F32 && out_dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
     if ((int64_t)batch * num_q_heads > 65535) return ATTN_ERR_UNSUPPORTED;

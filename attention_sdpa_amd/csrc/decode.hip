@@ -278,9 +278,10 @@ decode_split_kernel(DecodeArgs a) {
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float p = fast_exp2(fmaf(sacc[mb][i], cl, -mc_new));
-                psum += p;
-                pb[mb >> 1][4 * (mb & 1) + i] = to16<T>(p);
+                // the row sum takes the rounded weight, the one P V uses
+                const T p = to16<T>(fast_exp2(fmaf(sacc[mb][i], cl, -mc_new)));
+                psum += (float)p;
+                pb[mb >> 1][4 * (mb & 1) + i] = p;
             }
         l_run = l_run * alpha + psum;
         m_run = m_new;

@@ -113,8 +113,9 @@ int kv_store_slots(const void *k, const void *v, void *k_cache, void *v_cache,
  *   cu_seqlens_q, cu_seqlens_k  [batch + 1] int32, nondecreasing, from 0
  *   max_seqlen_q, max_seqlen_k  upper bounds of Lq_b, Lk_b (host ints; they
  *                size the launch, rows beyond max_seqlen_q are not computed)
- *   softmax_scale  s >= 0 (usually 1/sqrt(head_dim)); negative or non-finite
- *                is rejected with ATTN_ERR_SHAPE
+ *   softmax_scale  s > 0 and finite (usually 1/sqrt(head_dim)), with
+ *                s * log2(e) at least FLT_MIN; anything else (0, negative,
+ *                non-finite, subnormal) is rejected with ATTN_ERR_SHAPE
  *   causal       nonzero = causal mask as above
  *
  * Supported: in_dtype ATTN_BF16 or ATTN_F16 with head_dim 128 (16-bit
@@ -207,7 +208,7 @@ size_t attn_decode_workspace_bytes(int batch, int num_q_heads, int num_kv_heads,
  *   o             [batch, num_q_heads, head_dim], out_dtype
  *   cache_seqlens [batch] int32
  *   block_table   [batch, max_blocks_per_seq] int32
- *   softmax_scale s >= 0, finite (else ATTN_ERR_SHAPE)
+ *   softmax_scale s > 0, as for attn_prefill_varlen (else ATTN_ERR_SHAPE)
  *   workspace     device scratch of at least attn_decode_workspace_bytes()
  *                 bytes, 256-byte aligned, not shared with a concurrent call
  *

@@ -74,10 +74,29 @@ def check_bf16_output(got_bf16: torch.Tensor, ref, what=""):
     mag = np.maximum(np.abs(ref_b), 2.0 ** -126)
     ulp = 2.0 ** (np.floor(np.log2(mag)) - 7)       # bf16: 8 significant bits
     bound = BF16_MAX_ABS + ulp
-    excess = np.abs(got - ref_b) - bound
-    log(f"  {what}: bf16-out max |diff| {np.abs(got - ref_b).max():.3e}, "
-        f"max excess over bound {excess.max():.3e}")
+    diff = np.abs(got - ref_b)
+    excess = diff - bound
+    mean = float(diff.mean()) if diff.size else 0.0
+    log(f"  {what}: bf16-out max |diff| {diff.max():.3e} mean |diff| {mean:.3e} "
+        f"(vs unrounded oracle {np.abs(got - ref).mean():.3e}), max excess over bound {excess.max():.3e}")
     assert np.all(excess <= 0), f"{what}: bf16 output outside 1e-2 + 1 ulp"
+    assert mean <= BF16_MEAN_ABS, f"{what}: bf16-out mean abs {mean:.3e} > {BF16_MEAN_ABS}"
+
+
+def unit_rows(total_q: int, hq: int, hkv: int, every: int, block: int = 64) -> np.ndarray:
+    """Flat (token * hq + head) rows of every `every`-th (query block, KV
+    head) unit of one sequence: block qb of KV head g is taken when
+    (qb - 2 g) mod every == 0, so each KV head contributes blocks spread
+    evenly over the whole sequence, and each taken unit is complete (all
+    `block` positions of all hq / hkv query heads of that KV head)."""
+    group = hq // hkv
+    rows = []
+    for g in range(hkv):
+        for qb in range((2 * g) % every, -(-total_q // block), every):
+            t = np.arange(qb * block, min((qb + 1) * block, total_q), dtype=np.int64)
+            for h in range(g * group, (g + 1) * group):
+                rows.append(t * hq + h)
+    return np.sort(np.concatenate(rows))
 
 
 def sample_rows(cu_q: torch.Tensor, hq: int, n: int, seed: int) -> np.ndarray:

@@ -238,3 +238,18 @@ def test_null_kv_only_without_keys(lib):
     assert prefill(lib, v=None, total_k=0, bt=P2, mbs=4, nb=4, bs=64) == E.ATTN_ERR_NULL   # paged: never
     assert padded(lib, k=None) == E.ATTN_ERR_NULL
     assert padded(lib, k=None, v=None, maxq=0, maxk=0) == E.ATTN_OK     # nothing to do at all
+
+
+def test_scale_must_be_positive(lib):
+    """The kernels form a masked weight as 2^(-inf * c - m) with c = s * log2(e),
+    which is 0 only for c > 0: a zero, negative, non-finite or subnormal scale
+    is rejected by every entry point before any launch."""
+    E = attn
+    for s in (0.0, -0.0, -0.5, float("nan"), float("inf"), float("-inf"), 1e-40):
+        assert prefill(lib, scale=s) == E.ATTN_ERR_SHAPE, s
+        assert decode(lib, scale=s) == E.ATTN_ERR_SHAPE, s
+        assert padded(lib, scale=s) == E.ATTN_ERR_SHAPE, s
+        assert unfused(lib, scale=s) == E.ATTN_ERR_SHAPE, s
+    # the smallest accepted scale: s * log2(e) is a normal float
+    assert padded(lib, scale=1e-37, maxq=0) == E.ATTN_OK
+

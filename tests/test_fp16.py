@@ -17,15 +17,11 @@ pytestmark = pytest.mark.gpu
 F16 = torch.float16
 
 
-def run_varlen(vl, causal=None, out_dtype=torch.float32, paged=None):
-    kw = {}
-    k, v = dev(vl.k), dev(vl.v)
-    cu_k = vl.cu_seqlens_k
-    if paged is not None:
-        k, v = paged
-    out = attn.attn_prefill_varlen(dev(vl.q), k, v, dev(vl.cu_seqlens_q), dev(cu_k), vl.max_seqlen_q,
-                                   vl.max_seqlen_k, vl.softmax_scale,
-                                   vl.causal if causal is None else causal, out_dtype=out_dtype, **kw)
+def run_varlen(vl, causal=None, out_dtype=torch.float32):
+    out = attn.attn_prefill_varlen(dev(vl.q), dev(vl.k), dev(vl.v), dev(vl.cu_seqlens_q),
+                                   dev(vl.cu_seqlens_k), vl.max_seqlen_q, vl.max_seqlen_k,
+                                   vl.softmax_scale, vl.causal if causal is None else causal,
+                                   out_dtype=out_dtype)
     torch.cuda.synchronize()
     return out
 
