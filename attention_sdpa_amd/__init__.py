@@ -23,7 +23,7 @@ ATTN_F32, ATTN_BF16, ATTN_F16 = 0, 1, 2
 # exported C symbols (kept in sync with include/attn.h by the CPU tests)
 SYMBOLS = ("attn_status_str", "attn_version", "kv_store_slots", "attn_prefill_varlen",
            "attn_decode_workspace_bytes", "attn_decode_paged", "attn_unfused_workspace_bytes",
-           "attn_prefill_unfused", "attn_prefill_padded")
+           "attn_prefill_unfused", "attn_prefill_padded", "attn_decode_paged_noalloc")
 
 
 class AttnError(RuntimeError):
@@ -61,6 +61,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, i32p, i32p, ci, ci, ci, ci, ci, ci, ci, cf,
                                       ci, ci, ci, vp, csz, vp]
     lib.attn_decode_paged.restype = ci
+    lib.attn_decode_paged_noalloc.argtypes = [vp, vp, vp, vp, i32p, i32p, ci, ci, ci, ci, ci, ci, ci,
+                                              cf, ci, ci, ci, vp]
+    lib.attn_decode_paged_noalloc.restype = ci
     lib.attn_prefill_padded.argtypes = [vp, vp, vp, vp, i32p, i32p, ci, ci, ci, ci, ci, ci, cf, ci, ci,
                                         ci, vp]
     lib.attn_prefill_padded.restype = ci
@@ -233,6 +236,37 @@ def attn_decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _i32(cache_seqlens), _i32(block_table),
         B, hq, hkv, d, mbs, nb, bs, float(softmax_scale), int(split_tokens), _dt(q), _dt(out),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def attn_decode_paged_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                              cache_seqlens: torch.Tensor, block_table: torch.Tensor, softmax_scale: float,
+                              split_tokens: int = 0, out: Optional[torch.Tensor] = None, out_dtype=None,
+                              stream=None) -> torch.Tensor:
+    """attn_decode_paged on the library's built-in scratch (no workspace;
+    the library call allocates nothing -- pass `out` to allocate nothing
+    here either).  Calls that overlap on one GPU race on that scratch."""
+    what = "attn_decode_paged_noalloc"
+    _need(q.dim() == 3, what, f"q must be [batch, Hq, d], got {tuple(q.shape)}")
+    B, hq, d = q.shape
+    _kv_pair(k_cache, v_cache, q, what)
+    _need(k_cache.dim() == 4, what, f"caches must be [num_blocks, block_size, Hkv, d], got {tuple(k_cache.shape)}")
+    nb, bs, hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    _index(cache_seqlens, B, what, "cache_seqlens")
+    _need(block_table.dim() == 2 and block_table.shape[0] >= B, what,
+          f"block_table must be [>= {B}, max_blocks_per_seq], got {tuple(block_table.shape)}")
+    if block_table.dtype != torch.int32:
+        raise TypeError(f"{what}: block_table must be int32")
+    mbs = block_table.shape[1]
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=out_dtype or q.dtype, device=q.device)
+    _need(tuple(out.shape) == (B, hq, d), what, f"out must be {(B, hq, d)}, got {tuple(out.shape)}")
+    _same_device(what, q, k_cache, v_cache, out, cache_seqlens, block_table)
+    lib = load_library()
+    _check(what, lib.attn_decode_paged_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _i32(cache_seqlens), _i32(block_table),
+        B, hq, hkv, d, mbs, nb, bs, float(softmax_scale), int(split_tokens), _dt(q), _dt(out),
+        _stream(stream)))
     return out
 
 

@@ -73,7 +73,7 @@ ATTN_API const char *attn_status_str(int status) {
         case ATTN_ERR_NULL: return "a required pointer is NULL";
         case ATTN_ERR_SHAPE: return "invalid or inconsistent sizes";
         case ATTN_ERR_UNSUPPORTED: return "unsupported dtype, head_dim, alignment or layout";
-        case ATTN_ERR_WORKSPACE: return "decode workspace missing or too small";
+        case ATTN_ERR_WORKSPACE: return "workspace missing, too small or unaligned, or larger than the built-in decode scratch";
         case ATTN_ERR_HIP: return "HIP runtime error";
         default: return "unknown status";
     }
@@ -301,6 +301,25 @@ ATTN_API int attn_decode_paged(const void *q, const void *k_cache, const void *v
     if (!workspace || workspace_bytes < L.total) return ATTN_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_ERR_WORKSPACE;
     return decode_launch(&a, L, workspace, stream);
+}
+
+ATTN_API int attn_decode_paged_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                       void *o, const int32_t *cache_seqlens,
+                                       const int32_t *block_table, int batch, int num_q_heads,
+                                       int num_kv_heads, int head_dim, int max_blocks_per_seq,
+                                       int num_blocks, int block_size, float softmax_scale,
+                                       int split_tokens, int in_dtype, int out_dtype, void *stream) {
+    attn::DecodeArgs a;
+    DecodeLayout L;
+    const int st = decode_prepare(q, k_cache, v_cache, o, cache_seqlens, block_table, batch, num_q_heads,
+                                  num_kv_heads, head_dim, max_blocks_per_seq, num_blocks, block_size,
+                                  softmax_scale, split_tokens, in_dtype, out_dtype, &a, &L);
+    if (st != ATTN_OK) return st;
+    // the workspace this call needs must fit the per-device scratch array
+    if (L.total > attn::kDecodeScratchBytes) return ATTN_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (attn::decode_scratch(&ws) != hipSuccess || ws == nullptr) return ATTN_ERR_HIP;
+    return decode_launch(&a, L, ws, stream);
 }
 
 namespace {

@@ -38,6 +38,8 @@
 //   of O^T += V^T P^T.  Both are read into registers before any arithmetic,
 //   and the next chunk's K and V loads are issued into the same buffers
 //   right then: a wavefront has a chunk in flight while it computes.
+#include <atomic>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -450,6 +452,33 @@ decode_combine_kernel(DecodeArgs a) {
 }
 
 }  // namespace
+
+// Scratch of the allocation-free decode entry point: the decode workspace
+// (partials, (m, d') pairs, first/last runs) in a file-scope device array.
+// Each GPU the library runs on holds its own copy until the process ends.
+// Host code must never pass `scratch` itself to a kernel (in host code the
+// name is a host-side stand-in): decode_scratch() looks up its address on the
+// current device once and caches it per device.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<void *> addr[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void *p = addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        // the device is current: its copy of the array is the one resolved
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        addr[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return hipSuccess;
+}
 
 int decode_runs(int hkv, int cus) {
     const int hb = heads_per_block(hkv);

@@ -83,6 +83,12 @@ struct DecodeArgs {
 int decode_runs(int hkv, int cus);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 
+// Size of the per-device scratch array behind the allocation-free decode
+// entry point, and its device address on the current device (resolved once
+// per device by symbol lookup, then cached).
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+hipError_t decode_scratch(void **ptr);
+
 // The unfused three-step baseline (logits, softmax and A V as separate
 // kernels with X and A in the workspace).
 struct UnfusedArgs {

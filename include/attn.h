@@ -231,6 +231,33 @@ int attn_decode_paged(const void *q, const void *k_cache, const void *v_cache,
                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * attn_decode_paged_noalloc -- attn_decode_paged without a workspace
+ * argument and without any allocation, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments (minus workspace),
+ * semantics, kernels and results as attn_decode_paged; the workspace is a
+ * scratch array of 32 MiB built into the library, one per GPU, resolved on
+ * the first call on each device and held until the process ends.
+ *
+ * Limit: the call must fit that scratch, i.e.
+ * attn_decode_workspace_bytes(batch, ...) <= 32 MiB (at 32 query heads and
+ * head_dim 128: batch <= 992); larger calls return ATTN_ERR_WORKSPACE and
+ * launch nothing.  Nothing in the scratch needs clearing (every word the
+ * merge reads is written by the same call).  All calls on one GPU share its
+ * scratch: calls that overlap in time on one GPU (different streams, or
+ * host threads without ordering) race and give wrong results; serialise
+ * them, e.g. on one stream.  No hipMalloc, hipFree or allocating library
+ * call is made.  Errors as attn_decode_paged, plus ATTN_ERR_HIP if the
+ * scratch address cannot be resolved.
+ */
+int attn_decode_paged_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                              void *o, const int32_t *cache_seqlens,
+                              const int32_t *block_table, int batch, int num_q_heads,
+                              int num_kv_heads, int head_dim, int max_blocks_per_seq,
+                              int num_blocks, int block_size, float softmax_scale,
+                              int split_tokens, int in_dtype, int out_dtype, void *stream);
+
+/*
  * attn_unfused_workspace_bytes -- bytes of device workspace
  * attn_prefill_unfused needs (0 if the sizes are invalid): the logits X as
  * fp32, then (256-byte aligned) the probabilities A as bf16, each laid out

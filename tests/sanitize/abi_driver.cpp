@@ -21,6 +21,7 @@ hipError_t launch_prefill_mfma(const VarlenArgs &, hipStream_t) { std::abort(); 
 hipError_t launch_decode(const DecodeArgs &, hipStream_t) { std::abort(); }
 hipError_t launch_unfused(const UnfusedArgs &, hipStream_t) { std::abort(); }
 int decode_runs(int, int) { std::abort(); }
+hipError_t decode_scratch(void **) { std::abort(); }
 int decode_head_blocks(int hkv) { return (hkv + 7) / 8; }
 }  // namespace attn
 
@@ -61,6 +62,10 @@ int main() {
                              need, nullptr), ATTN_ERR_UNSUPPORTED, "decode split");
     expect(attn_decode_paged(P, P, P, P, I, I, 4, 64, 2, 128, 32, 200, 256, 0.1f, 0, ATTN_BF16, ATTN_F32, P,
                              need, nullptr), ATTN_ERR_UNSUPPORTED, "decode group");
+    expect(attn_decode_paged_noalloc(P, P, P, P, I, I, 993, 32, 8, 128, 32, 200, 256, 0.1f, 0, ATTN_BF16,
+                                     ATTN_F32, nullptr), ATTN_ERR_WORKSPACE, "decode noalloc beyond scratch");
+    expect(attn_decode_paged_noalloc(P, P, P, P, I, I, 4, 32, 8, 128, 32, 200, 256, 0.f, 0, ATTN_BF16,
+                                     ATTN_F32, nullptr), ATTN_ERR_SHAPE, "decode noalloc scale");
     const size_t uneed = attn_unfused_workspace_bytes(2, 32, 16, 16);
     expect(attn_prefill_unfused(P, P, P, P, I, I, 2, 16, 16, 20, 20, 32, 8, 128, 0.1f, 1, ATTN_BF16, ATTN_F32, P,
                                 uneed - 1, nullptr), ATTN_ERR_WORKSPACE, "unfused workspace");

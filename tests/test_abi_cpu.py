@@ -253,3 +253,28 @@ def test_scale_must_be_positive(lib):
     # the smallest accepted scale: s * log2(e) is a normal float
     assert padded(lib, scale=1e-37, maxq=0) == E.ATTN_OK
 
+
+def decode_noalloc(lib, **kw):
+    a = dict(q=P, kc=P, vc=P, o=P, sl=P2, bt=P2, batch=64, hq=32, hkv=8, d=128, mbs=32, nb=1120, bs=256,
+             scale=0.088, split=0, idt=attn.ATTN_BF16, odt=attn.ATTN_F32)
+    a.update(kw)
+    return lib.attn_decode_paged_noalloc(a["q"], a["kc"], a["vc"], a["o"], a["sl"], a["bt"], a["batch"],
+                                         a["hq"], a["hkv"], a["d"], a["mbs"], a["nb"], a["bs"], a["scale"],
+                                         a["split"], a["idt"], a["odt"], None)
+
+
+def test_decode_noalloc_validation(lib):
+    """The allocation-free decode validates like attn_decode_paged and
+    rejects calls whose workspace would exceed its 32 MiB scratch, all before
+    touching the HIP runtime."""
+    E = attn
+    assert decode_noalloc(lib, q=None) == E.ATTN_ERR_NULL
+    assert decode_noalloc(lib, hq=12, hkv=8) == E.ATTN_ERR_SHAPE
+    assert decode_noalloc(lib, scale=0.0) == E.ATTN_ERR_SHAPE
+    assert decode_noalloc(lib, d=64) == E.ATTN_ERR_UNSUPPORTED
+    assert decode_noalloc(lib, split=48) == E.ATTN_ERR_UNSUPPORTED
+    limit = 32 << 20
+    assert lib.attn_decode_workspace_bytes(992, 32, 8, 128, 32, 256, 0) <= limit
+    assert lib.attn_decode_workspace_bytes(993, 32, 8, 128, 32, 256, 0) > limit
+    assert decode_noalloc(lib, batch=993) == E.ATTN_ERR_WORKSPACE
+    assert decode_noalloc(lib, batch=4096) == E.ATTN_ERR_WORKSPACE
