@@ -57,10 +57,19 @@ __device__ __forceinline__ int swz_dv(int row) { return (row & 7) << 1; }
 // ... and of a K row (conflict-free 16-byte reads of 16 consecutive rows)
 __device__ __forceinline__ int swz_dk(int row) { return row & 15; }
 
-// Waits written as asm with a memory clobber, so that the compiler moves no
-// memory access across them: every vector-memory and LDS access (including
-// the direct-to-LDS loads) / every LDS and scalar access is complete.
-__device__ __forceinline__ void wait_all() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); }
+// Waits with a memory clobber, so that the compiler moves no memory access
+// across them: every vector-memory and LDS access (including the
+// direct-to-LDS loads) / every LDS and scalar access is complete.  The full
+// wait is the s_waitcnt builtin, not asm text, so that the compiler's own
+// wait tracking sees it too: it then knows the query fragments (ordinary
+// loads) have landed and adds no wait for them before the MFMAs -- a wait
+// that, counted by the hardware, would also cover the next chunk's
+// direct-to-LDS loads issued just before and serialise them with the math.
+__device__ __forceinline__ void wait_all() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);     // vmcnt(0) expcnt(0) lgkmcnt(0)
+    asm volatile("" ::: "memory");
+}
 __device__ __forceinline__ void wait_lgkm() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ void wave_sync_lds() {
