@@ -104,6 +104,33 @@ __device__ __forceinline__ void lds_dma16(const void *sbase, uint32_t voff, uint
         : "memory");
 }
 
+// Four such loads into consecutive LDS blocks of STEP bytes (lds, lds +
+// STEP, ...), lane offsets o0..o3 from one scalar base, with M0 saved and
+// restored once for the four.
+template <int STEP>
+__device__ __forceinline__ void lds_dma16x4(const void *sbase, uint32_t o0, uint32_t o1, uint32_t o2,
+                                            uint32_t o3, uint32_t lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %5\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %6\n\t"
+        "s_add_u32 m0, m0, %7\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %6\n\t"
+        "s_add_u32 m0, m0, %7\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %3, %6\n\t"
+        "s_add_u32 m0, m0, %7\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %4, %6\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(o0), "v"(o1), "v"(o2), "v"(o3), "s"(lds), "s"(sbase), "i"(STEP)
+        : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(const ATTN_LDS void *)p;
 }

@@ -327,6 +327,7 @@ struct KvCursor {
     int bt_i;           // paged: block-table index of the tile
     int in_blk;         // paged: the tile's offset inside its block
     int blk;            // paged: the tile's block id (validated)
+    const bf16 *src;    // this wave's tensor at the tile's first key, head g
 };
 
 // Per-wave view of a unit: the query head, this lane's query position and
@@ -545,6 +546,11 @@ prefill_mfma_kernel(VarlenArgs a, Geo geo) {
         return (blk >= 0 && blk < a.num_blocks) ? blk : 0;   // bad id: stay in bounds
     };
     KvCursor KU;                                           // this wave's load cursor
+    auto set_src = [&]() ATTN_INLINE {
+        const int tok = paged ? KU.blk * a.block_size + KU.in_blk : KU.tok;
+        KU.src = my_src + ((int64_t)tok * a.hkv + KU.g) * (int64_t)kD;
+    };
+    const int64_t tile_stride = (int64_t)kBN * a.hkv * kD;   // elements between consecutive tiles
     auto cursor_to = [&](const Unit &u) ATTN_INLINE {
         KU.k = u.k;
         KU.valid = u.valid;
@@ -559,6 +565,7 @@ prefill_mfma_kernel(VarlenArgs a, Geo geo) {
             KU.in_blk = 0;
             KU.blk = load_blk(KU.bt_row);
         }
+        if (u.valid) set_src();
     };
     cursor_to(C);
     auto advance = [&]() ATTN_INLINE {
@@ -566,12 +573,14 @@ prefill_mfma_kernel(VarlenArgs a, Geo geo) {
             cursor_to(find_unit(KU.k + 1, true));
         } else {
             KU.tok += kBN;
+            KU.src += tile_stride;            // the next rows of the same block, or of k/v
             if (paged) {
                 KU.in_blk += kBN;
                 if (KU.in_blk >= a.block_size) {
                     KU.in_blk = 0;
                     ++KU.bt_i;
                     KU.blk = load_blk(KU.bt_row + KU.bt_i);
+                    set_src();
                 }
             }
         }
@@ -585,17 +594,15 @@ prefill_mfma_kernel(VarlenArgs a, Geo geo) {
     auto issue = [&]() ATTN_INLINE {
         last_n = 0;
         if (KU.valid) {
-            const int tok = paged ? KU.blk * a.block_size + KU.in_blk : KU.tok;
             const int lim = min(kBN - 1, KU.kv_end - 1 - KU.t * kBN);
-            const bf16 *src = my_src + ((int64_t)tok * a.hkv + KU.g) * (int64_t)kD;
             const uint32_t lds = my_lds0 + my_stage * kStageBytes;
             if (lim == kBN - 1) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) lds_dma16(src, full[i], lds + 4 * i * kD * 2);
+                lds_dma16x4<4 * kD * 2>(KU.src, full[0], full[1], full[2], full[3], lds);
             } else {
+                uint32_t off[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    lds_dma16(src, (uint32_t)min(rr0 + 4 * i, lim) * row_bytes + chk[i], lds + 4 * i * kD * 2);
+                for (int i = 0; i < 4; ++i) off[i] = (uint32_t)min(rr0 + 4 * i, lim) * row_bytes + chk[i];
+                lds_dma16x4<4 * kD * 2>(KU.src, off[0], off[1], off[2], off[3], lds);
             }
             advance();
             last_n = 4;
