@@ -341,7 +341,7 @@ struct WaveView {
     bool row_valid;
 };
 
-template <typename T, bool kListed>
+template <typename T, bool kListed, bool kPaged>
 __global__ void __launch_bounds__(kThreads, 1)
 prefill_mfma_kernel(VarlenArgs a, Geo geo) {
     typedef typename Vec16<T>::x2 T2;
@@ -371,7 +371,7 @@ prefill_mfma_kernel(VarlenArgs a, Geo geo) {
     const int hf = lane >> 5;                          // lane half
     const float cl = a.scale_log2;
     const int dr = lane >> 4, dc = lane & 15;
-    const bool paged = a.block_table != nullptr;
+    constexpr bool paged = kPaged;                         // K/V through the block table
 
     // ---- listed schedule: this workgroup's units --------------------------
     // Units are sorted by cost (their K/V tile count), heaviest first, and
@@ -613,6 +613,10 @@ prefill_mfma_kernel(VarlenArgs a, Geo geo) {
     // The wait of this wave's next waiting barrier: the vector-memory
     // operations (vm_allow, below) it may leave outstanding.
     auto wait_barrier = [&]() ATTN_INLINE {
+        if (vm_allow == 4) {                               // the steady state: one batch in flight
+            stage_barrier<kWaitVm4>();
+            return;
+        }
         switch (vm_allow) {
             case 4: stage_barrier<kWaitVm4>(); break;
             case 8: stage_barrier<kWaitVm8>(); break;
@@ -949,14 +953,21 @@ hipError_t launch_prefill_typed(const VarlenArgs &a, hipStream_t stream) {
     const int64_t grid_l = units_max < cus ? units_max : cus;
     const bool listed = a.batch <= kMaxBatchListed && geo.nqt <= kMaxRowsListed && a.hkv <= 256 &&
                         geo.head_chunks <= 256 && (units_max + grid_l - 1) / grid_l <= kMaxUnitsListed;
+    const bool paged = a.block_table != nullptr;
     if (listed) {
-        hipLaunchKernelGGL((prefill_mfma_kernel<T, true>), dim3((unsigned)grid_l), dim3(kThreads), 0, stream, a, geo);
+        if (paged)
+            hipLaunchKernelGGL((prefill_mfma_kernel<T, true, true>), dim3((unsigned)grid_l), dim3(kThreads), 0, stream, a, geo);
+        else
+            hipLaunchKernelGGL((prefill_mfma_kernel<T, true, false>), dim3((unsigned)grid_l), dim3(kThreads), 0, stream, a, geo);
     } else {
         // a multiple of the padded KV-head count keeps each workgroup on one head
         int64_t grid = geo.slots < (int64_t)cus ? geo.slots : (int64_t)cus;
         const int g2 = 1 << geo.lg;
         if (grid > g2) grid -= grid % g2;
-        hipLaunchKernelGGL((prefill_mfma_kernel<T, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a, geo);
+        if (paged)
+            hipLaunchKernelGGL((prefill_mfma_kernel<T, false, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a, geo);
+        else
+            hipLaunchKernelGGL((prefill_mfma_kernel<T, false, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a, geo);
     }
     return hipGetLastError();
 }
