@@ -77,6 +77,18 @@ constexpr int kD = 128;
 constexpr int kTileElems = kBN * kD;
 constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
 
+// x = -inf when key offset c >= thr: one compare and one select per key.
+// (Written as asm: the compiler otherwise turns the 16 compares of a block,
+// whose constants increase, into a serial chain of scalar ORs.)
+__device__ __forceinline__ float mask_key(float x, int thr, int c) {
+    asm("v_cmp_le_i32 vcc, %1, %2\n\t"
+        "v_cndmask_b32 %0, %0, %3, vcc"
+        : "+v"(x)
+        : "v"(thr), "i"(c), "v"(kNegInf)
+        : "vcc");
+    return x;
+}
+
 // Swap bits 2 and 3: the key order inside a 32-key block.
 __device__ __forceinline__ int perm23(int m) {
     return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
@@ -784,10 +796,6 @@ prefill_mfma_kernel(VarlenArgs a, Geo geo) {
                 const int jj = i >> 2, db = i & 3;
                 o[db] = mfma_32x32x16(vbuf[i], pb[jj], o[db]);
                 if (i + kAhead < 16) read_v(i + kAhead);
-                T2 pr;
-                pr[0] = pb[jj][2 * db];
-                pr[1] = pb[jj][2 * db + 1];
-                l_run = dot2_acc(pr, ones2, l_run);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
@@ -803,8 +811,7 @@ prefill_mfma_kernel(VarlenArgs a, Geo geo) {
                 for (int kb = 0; kb < 2; ++kb) {
                     const int thr = V.lim - t0 - 32 * kb - 8 * hf;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        if ((i < 8 ? i : i + 8) >= thr) sacc[kb][i] = kNegInf;
+                    for (int i = 0; i < 16; ++i) sacc[kb][i] = mask_key(sacc[kb][i], thr, i < 8 ? i : i + 8);
                 }
             }
             float mx = kNegInf;
@@ -814,7 +821,8 @@ prefill_mfma_kernel(VarlenArgs a, Geo geo) {
                 for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
             mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-            const bool need = mx > m_ref && (m_ref == kNegInf || mx * cl > mc_ref + kRescaleLog2);
+            // straight-line (no short-circuit, so no exec-mask branches)
+            const bool need = (mx > m_ref) & ((m_ref == kNegInf) | (mx * cl > mc_ref + kRescaleLog2));
             if (__builtin_amdgcn_ballot_w64(need)) {
                 const float m_new = fmaxf(m_ref, mx);
                 const float mc_new = (m_new == kNegInf) ? 0.f : m_new * cl;
@@ -834,6 +842,21 @@ prefill_mfma_kernel(VarlenArgs a, Geo geo) {
                     pb[2 * kb + (i >> 3)][i & 7] = to16<T>(fast_exp2(fmaf(sacc[kb][i], cl, -mc_ref)));
         };
 
+        // d' += the row sums of the weights the last P V used (the bf16-rounded
+        // ones), at the start of the following softmax phase: there they fill
+        // the wait for the matrix phase's last results (measured: 6 % faster
+        // than beside the MFMAs, 8 % faster than after the exponentials)
+        auto sum_p = [&]() ATTN_INLINE {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    T2 pr;
+                    pr[0] = pb[jj][2 * e];
+                    pr[1] = pb[jj][2 * e + 1];
+                    l_run = dot2_acc(pr, ones2, l_run);
+                }
+        };
         auto zero_p = [&]() ATTN_INLINE {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) pb[jj] = T8{};
@@ -888,6 +911,7 @@ prefill_mfma_kernel(VarlenArgs a, Geo geo) {
             __builtin_amdgcn_s_setprio(0);
             if (grpA) odd_barrier();
             else even_barrier();
+            sum_p();
             if (t + 1 < V.nw) softmax(t + 1);
             else zero_p();
             st = st1;
@@ -900,6 +924,7 @@ prefill_mfma_kernel(VarlenArgs a, Geo geo) {
             __builtin_amdgcn_s_setprio(1);
             mma(st1, st, std::false_type{});
             __builtin_amdgcn_s_setprio(0);
+            sum_p();
             Cn = find_unit(C.k + 1, false);
             skip_empty(Cn);
             if (Cn.valid) load_q(Cn);                      // before the batch: the next wait covers it
