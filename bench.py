@@ -19,8 +19,10 @@ the paged cache (kv_store_slots), then attention.
   roofline, the oracle's rate on a sample of the batch (cpu_baseline), and
   the shared-prompt decode variant (64 sequences whose block tables begin
   with the same 8 physical blocks).
-* roofline: the prefill kernel alone, from events recorded around each of
-  its launches inside the timed region, against bf16 dense MFMA peak;
+* roofline: the prefill kernel alone, timed right after the steps as K
+  launches back to back between two HIP events (no store between them; the
+  steps themselves carry no events, whose records leave the GPU idle for a
+  few microseconds each), against bf16 dense MFMA peak;
   traffic = HBM bytes per launch from the FETCH_SIZE / WRITE_SIZE counter
   runs recorded in profiles/ (null once the kernel sources changed).
 * other_prefill: the 32768-token sequence, the prefix-cache batch (32
@@ -138,23 +140,36 @@ def visible_pairs(cu_q, cu_k, causal=True) -> int:
     return total
 
 
-def timed_loop(step, steps, warmup, torch, inner=None):
+def timed_loop(step, steps, warmup, torch):
     """W untimed steps, then K timed steps between a device sync on both
-    sides.  inner(i) returns (start_event, end_event) pairs recorded around
-    the kernel of interest inside step i."""
+    sides; returns the wall time of the K steps in seconds.  Nothing else is
+    enqueued between the steps (no events: each one recorded between two
+    launches leaves the GPU idle for several microseconds)."""
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    pairs = []
     t0 = time.perf_counter()
     for i in range(steps):
-        p = step(i)
-        if p is not None:
-            pairs.append(p)
+        step(i)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kernel_ms = [a.elapsed_time(b) for a, b in pairs]
-    return wall, kernel_ms
+    return time.perf_counter() - t0
+
+
+def launch_ms(call, steps, warmup, torch):
+    """Average duration in ms of one launch of `call` (an attention entry
+    point): W untimed calls, then K calls back to back between two HIP
+    events on torch's current stream, which is the stream the library
+    launches on."""
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
 
 
 def shared_prefill_workload(workloads, dtype, queries=(1, 512), n_seqs=32, own_hi=4096, seed=1006):
@@ -192,23 +207,21 @@ def prep_prefix(args, torch, attn, workloads):
     kn, vn, slots = pg.k_new.cuda(), pg.v_new.cuda(), pg.slot_mapping.cuda()
     cu_q, cu_k, bt = pp.cu_seqlens_q.cuda(), pg.cu_seqlens_k.cuda(), pg.block_table.cuda()
     out = torch.empty_like(q)
-    Ev = torch.cuda.Event
+
+    def call():
+        attn.attn_prefill_varlen(q, kc, vc, cu_q, cu_k, pp.max_seqlen_q, pp.max_seqlen_k,
+                                 pp.softmax_scale, True, block_table=bt, out=out)
 
     def step(i):
         attn.kv_store_slots(kn, vn, kc, vc, slots)
-        e0, e1 = Ev(enable_timing=True), Ev(enable_timing=True)
-        e0.record()
-        attn.attn_prefill_varlen(q, kc, vc, cu_q, cu_k, pp.max_seqlen_q, pp.max_seqlen_k,
-                                 pp.softmax_scale, True, block_table=bt, out=out)
-        e1.record()
-        return e0, e1
+        call()
 
     def go():
-        wall, kms = timed_loop(step, args.steps, args.warmup, torch)
+        wall = timed_loop(step, args.steps, args.warmup, torch)
+        k_ms = launch_ms(call, args.steps, args.warmup, torch)
         pairs = visible_pairs(pp.cu_seqlens_q.tolist(), pg.cu_seqlens_k.tolist(), True)
         flops = 4.0 * 128 * 32 * pairs
         ms_step = wall * 1e3 / args.steps
-        k_ms = sum(kms) / len(kms)
         total_k = int(pg.cu_seqlens_k[-1])
         bound_s = per_sequence_bound(pp.cu_seqlens_q.tolist(), pg.cu_seqlens_k.tolist())
         return dict(vl=None, flops=flops, ms_step=ms_step, kernel_ms=k_ms,
@@ -237,27 +250,21 @@ def prep_prefill(args, torch, attn, workloads):
     kc, vc = cache.k_cache.cuda(), cache.v_cache.cuda()
     slots = cache.slot_mapping.cuda()
     out = torch.empty_like(q)
-    Ev = torch.cuda.Event
-
-    def step(i):
-        attn.kv_store_slots(k, v, kc, vc, slots)
-        e0, e1 = Ev(enable_timing=True), Ev(enable_timing=True)
-        e0.record()
-        attn.attn_prefill_varlen(q, k, v, cu_q, cu_k, vl.max_seqlen_q, vl.max_seqlen_k,
-                                 vl.softmax_scale, vl.causal, out=out)
-        e1.record()
-        return e0, e1
 
     def enqueue():
         attn.attn_prefill_varlen(q, k, v, cu_q, cu_k, vl.max_seqlen_q, vl.max_seqlen_k,
                                  vl.softmax_scale, vl.causal, out=out)
 
+    def step(i):
+        attn.kv_store_slots(k, v, kc, vc, slots)
+        enqueue()
+
     def go():
-        wall, kms = timed_loop(step, args.steps, args.warmup, torch)
+        wall = timed_loop(step, args.steps, args.warmup, torch)
+        k_ms = launch_ms(enqueue, args.steps, args.warmup, torch)
         pairs = visible_pairs(vl.cu_seqlens_q.tolist(), vl.cu_seqlens_k.tolist(), vl.causal)
         flops = 4.0 * 128 * 32 * pairs
         ms_step = wall * 1e3 / args.steps
-        k_ms = sum(kms) / len(kms)
         lens = (vl.cu_seqlens_q[1:] - vl.cu_seqlens_q[:-1]).tolist()
         return dict(vl=vl, flops=flops, ms_step=ms_step, kernel_ms=k_ms,
                     tflops_step=flops / (ms_step * 1e-3) / 1e12,
@@ -286,21 +293,19 @@ def prep_decode(args, torch, attn, workloads, shared=False):
     out = torch.empty_like(q)
     need = attn.attn_decode_workspace_bytes(q.shape[0], 32, 8, 128, bt.shape[1], 256, 0)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
-    Ev = torch.cuda.Event
+
+    def call():
+        attn.attn_decode_paged(q, kc, vc, sl, bt, dc.softmax_scale, workspace=ws, out=out)
 
     def step(i):
         attn.kv_store_slots(kn, vn, kc, vc, slots)
-        e0, e1 = Ev(enable_timing=True), Ev(enable_timing=True)
-        e0.record()
-        attn.attn_decode_paged(q, kc, vc, sl, bt, dc.softmax_scale, workspace=ws, out=out)
-        e1.record()
-        return e0, e1
+        call()
 
     def go():
-        wall, kms = timed_loop(step, args.steps, args.warmup, torch)
+        wall = timed_loop(step, args.steps, args.warmup, torch)
+        k_ms = launch_ms(call, args.steps, args.warmup, torch)
         kv_bytes = float(sum(pg.seqlens_k.tolist())) * 8 * 128 * 2 * 2
         ms_step = wall * 1e3 / args.steps
-        k_ms = sum(kms) / len(kms)
         return dict(dc=dc, kv_bytes=kv_bytes, ms_step=ms_step, kernel_ms=k_ms,
                     gbs_step=kv_bytes / (ms_step * 1e-3) / 1e9,
                     gbs_kernel=kv_bytes / (k_ms * 1e-3) / 1e9,
@@ -318,22 +323,16 @@ def prep_unfused(args, torch, attn, workloads):
     out = torch.empty_like(q)
     B = vl.cu_seqlens_q.numel() - 1
     need = attn.attn_unfused_workspace_bytes(B, 32, vl.max_seqlen_q, vl.max_seqlen_k)
-    Ev = torch.cuda.Event
 
     def go(fused_ms):
         ws = torch.empty(need, dtype=torch.uint8, device="cuda")
 
-        def step(i):
-            e0, e1 = Ev(enable_timing=True), Ev(enable_timing=True)
-            e0.record()
+        def call():
             attn.attn_prefill_unfused(q, k, v, cu_q, cu_k, vl.max_seqlen_q, vl.max_seqlen_k,
                                       vl.softmax_scale, True, workspace=ws, out=out)
-            e1.record()
-            return e0, e1
 
         steps, warmup = max(1, min(args.steps, 10)), max(1, min(args.warmup, 2))
-        _, kms = timed_loop(step, steps, warmup, torch)
-        ms = sum(kms) / len(kms)
+        ms = launch_ms(call, steps, warmup, torch)
         lq = (vl.cu_seqlens_q[1:] - vl.cu_seqlens_q[:-1]).tolist()
         lk = (vl.cu_seqlens_k[1:] - vl.cu_seqlens_k[:-1]).tolist()
         pairs_all = float(sum(a * b for a, b in zip(lq, lk)))
