@@ -25,9 +25,11 @@
  * - Values that live in device memory (cu_seqlens, block tables, slot
  *   mappings, cache lengths) are preconditions the host cannot check without
  *   a sync.  The kernels bound every access by the sizes passed here: a
- *   block id outside [0, num_blocks) reads as a zero row, a slot outside the
- *   cache is skipped, and a sequence range outside [0, total) is clipped, so
- *   bad metadata gives wrong numbers, never an out-of-bounds access.
+ *   block id outside [0, num_blocks) reads as zero rows in decode and in the
+ *   fp32 prefill, and as physical block 0 in the bf16/fp16 prefill; a slot
+ *   outside the cache is skipped; a sequence range outside [0, total) is
+ *   clipped.  Bad metadata gives wrong numbers, never an out-of-bounds
+ *   access.
  * - dtype codes: ATTN_F32 (IEEE binary32), ATTN_BF16 (bfloat16) and ATTN_F16
  *   (IEEE binary16).
  * - Grouped-query attention: query head h reads KV head h / (Hq / Hkv).

@@ -161,6 +161,38 @@ def test_decode_reused_workspace():
         check_bf16(np32(got), oracle_decode(dc), f"decode reused workspace call {i}")
 
 
+def test_decode_block_ids_outside_the_pool():
+    """A block id outside [0, num_blocks) reads as zero rows.  Many short
+    sequences put sequence boundaries inside runs, and the bad ids include
+    first blocks, which the split kernel requests for the next sequence while
+    it finishes the previous one."""
+    rng = np.random.default_rng(61)
+    ctx = [int(c) for c in rng.integers(100, 900, size=48)]
+    dc = make_decode(ctx, block_size=64, seed=62)
+    pg = dc.paged
+    nb = pg.num_blocks
+    bad = [(b, 0, -1 if b % 2 else nb + b) for b in range(0, 48, 3)]
+    bad += [(b, (ctx[b] + 63) // 64 // 2, nb) for b in range(1, 48, 5) if (ctx[b] + 63) // 64 > 2]
+    # the block of the new token (the last of each context) stays valid
+    assert all(i != (ctx[b] - 1) // 64 for b, i, _ in bad)
+    bt = pg.block_table.clone()
+    k, v = pg.k_logical.clone(), pg.v_logical.clone()
+    cu = pg.cu_seqlens_k.tolist()
+    for b, i, blk in bad:
+        bt[b, i] = blk
+        lo, hi = cu[b] + 64 * i, min(cu[b] + 64 * (i + 1), cu[b + 1])
+        k[lo:hi] = 0
+        v[lo:hi] = 0
+    kc, vc = dev(pg.k_cache), dev(pg.v_cache)
+    attn.kv_store_slots(dev(pg.k_new), dev(pg.v_new), kc, vc, dev(pg.slot_mapping))
+    log("case decode block ids outside the pool")
+    got = attn.attn_decode_paged(dev(dc.q), kc, vc, dev(pg.seqlens_k), dev(bt), dc.softmax_scale,
+                                 out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.attn_decode(np32(dc.q), np32(k), np32(v), pg.cu_seqlens_k.numpy(), dc.softmax_scale)
+    check_bf16(np32(got), ref, "decode bad block ids")
+
+
 def test_decode_all_contexts_empty():
     """Every context length 0: the key stream has no item at all, no run is
     used, and every output row is 0."""

@@ -214,6 +214,84 @@ def test_fp32_paged_matches_oracle():
     check_f32(np32(run_prefix(pp)), oracle_prefix(pp), "fp32 paged")
 
 
+def test_bf16_paged_many_sequences():
+    """Paged K/V with more sequences than the schedule tables hold (1100 >
+    1024): the launch takes the strided unit schedule through the block
+    table; cached prefixes include empty ones."""
+    pp = workloads.prefix_prefill(n_seqs=1100, q_lo=1, q_hi=24, p_lo=0, p_hi=90, hq=4, hkv=2,
+                                  block_size=64, seed=91)
+    log("case bf16 paged 1100 sequences (strided schedule)")
+    check_bf16(np32(run_prefix(pp)), oracle_prefix(pp), "bf16 paged 1100 seqs")
+
+
+def bad_block_case(pp, picks):
+    """Block table with the (sequence, block index, id) picks applied, and the
+    list of (first row, end row) logical ranges they cover."""
+    pg = pp.paged
+    bt = pg.block_table.clone()
+    cu = pg.cu_seqlens_k.tolist()
+    bs = pg.block_size
+    ranges = []
+    for b, i, blk in picks:
+        assert cu[b] + bs * i < cu[b + 1], "the pick must be one of the sequence's blocks"
+        bt[b, i] = blk
+        ranges.append((b, i, cu[b] + bs * i, min(cu[b] + bs * (i + 1), cu[b + 1])))
+    return bt, ranges
+
+
+def test_fp32_paged_block_ids_outside_the_pool():
+    """fp32 prefill: a block id outside [0, num_blocks) reads as zero rows."""
+    pp = workloads.prefix_prefill(n_seqs=4, q_lo=5, q_hi=40, p_lo=60, p_hi=200, hq=4, hkv=2, d=64,
+                                  block_size=16, seed=81, dtype=torch.float32)
+    pg = pp.paged
+    nb = pg.num_blocks
+    bt, ranges = bad_block_case(pp, [(0, 0, -1), (1, 2, nb), (3, 1, nb + 4)])
+    k, v = pg.k_logical.clone(), pg.v_logical.clone()
+    for _, _, lo, hi in ranges:
+        k[lo:hi] = 0
+        v[lo:hi] = 0
+    kc, vc = dev(pg.k_cache), dev(pg.v_cache)
+    attn.kv_store_slots(dev(pg.k_new), dev(pg.v_new), kc, vc, dev(pg.slot_mapping))
+    log("case fp32 paged block ids outside the pool")
+    got = attn.attn_prefill_varlen(dev(pp.q), kc, vc, dev(pp.cu_seqlens_q), dev(pg.cu_seqlens_k),
+                                   pp.max_seqlen_q, pp.max_seqlen_k, pp.softmax_scale, True,
+                                   block_table=dev(bt), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.attn_varlen(np32(pp.q), np32(k), np32(v), pp.cu_seqlens_q.numpy(),
+                             pg.cu_seqlens_k.numpy(), pp.softmax_scale, True)
+    check_f32(np32(got), ref, "fp32 paged bad block ids")
+
+
+def test_bf16_paged_block_ids_outside_the_pool():
+    """Matrix-core prefill: a block id outside [0, num_blocks) is read as
+    physical block 0 (the access stays inside the cache), and sequences whose
+    tables are valid are unaffected."""
+    pp = workloads.prefix_prefill(n_seqs=6, q_lo=20, q_hi=150, p_lo=200, p_hi=700, hq=8, hkv=2,
+                                  block_size=64, seed=71)
+    pg = pp.paged
+    nb = pg.num_blocks
+    bt, ranges = bad_block_case(pp, [(1, 0, -1), (1, 3, nb), (4, 1, nb + 9), (5, 2, -7)])
+    kc, vc = dev(pg.k_cache), dev(pg.v_cache)
+    attn.kv_store_slots(dev(pg.k_new), dev(pg.v_new), kc, vc, dev(pg.slot_mapping))
+    # slots of block 0 that no sequence uses hold the NaN sentinel; give them
+    # finite values (no valid table reaches them)
+    kc[0] = torch.nan_to_num(kc[0], nan=0.25)
+    vc[0] = torch.nan_to_num(vc[0], nan=-0.5)
+    k0, v0 = kc[0].cpu(), vc[0].cpu()
+    k, v = pg.k_logical.clone(), pg.v_logical.clone()
+    for _, _, lo, hi in ranges:
+        k[lo:hi] = k0[:hi - lo]
+        v[lo:hi] = v0[:hi - lo]
+    log("case bf16 paged block ids outside the pool")
+    got = attn.attn_prefill_varlen(dev(pp.q), kc, vc, dev(pp.cu_seqlens_q), dev(pg.cu_seqlens_k),
+                                   pp.max_seqlen_q, pp.max_seqlen_k, pp.softmax_scale, True,
+                                   block_table=dev(bt), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.attn_varlen(np32(pp.q), np32(k), np32(v), pp.cu_seqlens_q.numpy(),
+                             pg.cu_seqlens_k.numpy(), pp.softmax_scale, True)
+    check_bf16(np32(got), ref, "bf16 paged bad block ids")
+
+
 # ---------------------------------------------------------------- full-size workloads
 # The benchmark's workloads in the benchmark's launch configuration (bf16
 # output), and again with fp32 output; the varlen and prefix-cache batches
