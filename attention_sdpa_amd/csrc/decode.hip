@@ -134,7 +134,7 @@ decode_split_kernel(DecodeArgs a) {
     if (w == 0) {
         auto items_of = [&](int b) ATTN_INLINE {
             int64_t c = 0;
-            if (b < a.batch) c = (seq_len(b) + S - 1) / S;
+            if (b < a.batch) c = ((int64_t)seq_len(b) + S - 1) / S;
             return c;
         };
         auto scan = [&](int64_t c) ATTN_INLINE {    // inclusive scan over the wave
@@ -392,12 +392,14 @@ decode_split_kernel(DecodeArgs a) {
     const bool direct = wpH == 1;
 
     int L = seq_len(b);
-    int ns = (L + S - 1) / S;
+    // item counts and item ends in 64 bits: S may be as large as the caller's
+    // item size allows (any positive multiple of 32)
+    int ns = (int)(((int64_t)L + S - 1) / S);
     bool pre = false;   // this segment's first chunk went out with the last one of the previous
     for (int it = 0; it < n_items;) {
         // segment: items s .. s + cnt - 1 of sequence b
         const int cnt = min(ns - s, n_items - it);
-        const int kbeg = s * S, kend = min(L, (s + cnt) * S);
+        const int kbeg = s * S, kend = (int)min((int64_t)L, (int64_t)(s + cnt) * S);
         if (hb == 0 && tid == 0) {
             if (s == 0) a.ws_runs[2 * b] = r;
             if (s + cnt == ns) a.ws_runs[2 * b + 1] = r;
@@ -409,11 +411,11 @@ decode_split_kernel(DecodeArgs a) {
             do {
                 ++bn;
                 Ln = bn < a.batch ? seq_len(bn) : 0;
-                nsn = (Ln + S - 1) / S;
+                nsn = (int)(((int64_t)Ln + S - 1) / S);
             } while (nsn == 0 && bn < a.batch);
         }
         const bool has_next = itn < n_items && bn < a.batch;
-        const int kendn = has_next ? min(Ln, min(nsn, n_items - itn) * S) : 0;
+        const int kendn = has_next ? (int)min((int64_t)Ln, (int64_t)min(nsn, n_items - itn) * S) : 0;
         m_run = kNegInf;
         mc_run = 0.f;
         l_run = 0.f;

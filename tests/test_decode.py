@@ -193,6 +193,15 @@ def test_decode_block_ids_outside_the_pool():
     check_bf16(np32(got), ref, "decode bad block ids")
 
 
+def test_decode_largest_item_size():
+    """split_tokens at the largest multiple of 32 an int holds: every
+    sequence is one item, and the item counts and ends (computed in 64 bits)
+    do not overflow."""
+    dc = make_decode([700, 1, 3000, 257], seed=71)
+    log("case decode split_tokens 2147483616")
+    check_bf16(np32(run_decode(dc, 2147483616)), oracle_decode(dc), "decode largest item size")
+
+
 def test_decode_all_contexts_empty():
     """Every context length 0: the key stream has no item at all, no run is
     used, and every output row is 0."""
