@@ -122,6 +122,8 @@ ATTN_API int attn_prefill_varlen(const void *q, const void *k, const void *v, vo
     const bool paged = block_table != nullptr;
     if (paged) {
         if (max_blocks_per_seq <= 0 || num_blocks <= 0 || block_size <= 0) return ATTN_ERR_SHAPE;
+        // the kernels form a cache slot (block * block_size + offset) in 32 bits
+        if ((int64_t)num_blocks * block_size > 0x7fffffffLL) return ATTN_ERR_SHAPE;
     } else if (total_k < 0) {
         return ATTN_ERR_SHAPE;
     }

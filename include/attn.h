@@ -107,7 +107,8 @@ int kv_store_slots(const void *k, const void *v, void *k_cache, void *v_cache,
  *       b is slot block_table[b * max_blocks_per_seq + j / block_size]
  *       * block_size + j % block_size.  total_k is ignored; Lk_b still comes
  *       from cu_seqlens_k.  Table entries past ceil(Lk_b / block_size) are
- *       never read.
+ *       never read.  num_blocks * block_size must fit a 32-bit int (else
+ *       ATTN_ERR_SHAPE).
  *
  *   q            [total_q, num_q_heads, head_dim], in_dtype
  *   o            [total_q, num_q_heads, head_dim], out_dtype (written only

@@ -84,6 +84,7 @@ def test_prefill_validation(lib):
     assert prefill(lib, q=MIS) == E.ATTN_ERR_UNSUPPORTED
     assert prefill(lib, bt=P2, mbs=0, nb=4, bs=256) == E.ATTN_ERR_SHAPE
     assert prefill(lib, bt=P2, mbs=4, nb=4, bs=100) == E.ATTN_ERR_UNSUPPORTED  # bf16 paged: bs % 64
+    assert prefill(lib, bt=P2, mbs=4, nb=1 << 24, bs=256) == E.ATTN_ERR_SHAPE   # 2^32 cache slots
     # nothing to do: valid arguments with zero query rows return OK without a launch
     assert prefill(lib, maxq=0) == E.ATTN_OK
     assert prefill(lib, total_q=0) == E.ATTN_OK
