@@ -56,8 +56,9 @@
 // * Exponentials in base 2 with c = s*log2(e): p = 2^(fma(x, c, -r*c)) for a
 //   per-row reference r.  r follows the running maximum lazily: it is raised
 //   (and o', d' rescaled by 2^(r_old*c - r_new*c), the same rounded
-//   products) only when the maximum exceeds it by more than 2^8, which keeps
-//   p <= 256 and leaves the result unchanged in exact arithmetic.
+//   products) only when the scaled maximum exceeds the scaled reference by
+//   more than 8 (x*c - r*c > 8), which keeps p <= 256 and leaves the result
+//   unchanged in exact arithmetic.
 // * Row sums are accumulated from the bf16-rounded P with v_dot2_f32_bf16,
 //   i.e. from exactly the weights the P V product uses.
 #include <type_traits>
