@@ -138,9 +138,20 @@ def _kv_pair(k: torch.Tensor, v: torch.Tensor, q: torch.Tensor, what: str):
           f"head_dim of k ({k.shape[-1]}) differs from q ({q.shape[-1]})")
 
 
-def _stream(stream=None):
-    s = torch.cuda.current_stream() if stream is None else stream
+def _stream(dev: torch.device, stream=None):
+    """The stream to enqueue on: the given one, which must belong to the
+    tensors' device, or that device's current torch stream."""
+    s = torch.cuda.current_stream(dev) if stream is None else stream
+    if s.device != dev:
+        raise ValueError(f"the stream is on {s.device}, the tensors on {dev}")
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _run(dev: torch.device, fn, *args):
+    """Call into the library with the tensors' device current: the library
+    launches on the current device and reads its properties there."""
+    with torch.cuda.device(dev):
+        return fn(*args)
 
 
 def kv_store_slots(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -156,9 +167,9 @@ def kv_store_slots(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor, v_ca
         raise TypeError("kv_store_slots: slot_mapping must be int32")
     _same_device("kv_store_slots", k, v, k_cache, v_cache, slot_mapping)
     lib = load_library()
-    _check("kv_store_slots", lib.kv_store_slots(
+    _check("kv_store_slots", _run(k.device, lib.kv_store_slots,
         _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _i32(slot_mapping), T, hkv, d, nb, bs,
-        _dt(k), _stream(stream)))
+        _dt(k), _stream(k.device, stream)))
 
 
 def attn_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
@@ -194,10 +205,10 @@ def attn_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     _need(tuple(out.shape) == (total_q, hq, d), what, f"out must be {(total_q, hq, d)}, got {tuple(out.shape)}")
     _same_device(what, q, k, v, out, cu_seqlens_q, cu_seqlens_k, block_table)
     lib = load_library()
-    _check("attn_prefill_varlen", lib.attn_prefill_varlen(
+    _check("attn_prefill_varlen", _run(q.device, lib.attn_prefill_varlen,
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _i32(cu_seqlens_q), _i32(cu_seqlens_k), batch,
         int(max_seqlen_q), int(max_seqlen_k), total_q, total_k, hq, hkv, d, float(softmax_scale),
-        int(bool(causal)), _i32(block_table), mbs, nb, bs, _dt(q), _dt(out), _stream(stream)))
+        int(bool(causal)), _i32(block_table), mbs, nb, bs, _dt(q), _dt(out), _stream(q.device, stream)))
     return out
 
 
@@ -232,10 +243,10 @@ def attn_decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _same_device(what, q, k_cache, v_cache, out, cache_seqlens, block_table, workspace)
     lib = load_library()
-    _check("attn_decode_paged", lib.attn_decode_paged(
+    _check("attn_decode_paged", _run(q.device, lib.attn_decode_paged,
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _i32(cache_seqlens), _i32(block_table),
         B, hq, hkv, d, mbs, nb, bs, float(softmax_scale), int(split_tokens), _dt(q), _dt(out),
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device, stream)))
     return out
 
 
@@ -263,10 +274,10 @@ def attn_decode_paged_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: t
     _need(tuple(out.shape) == (B, hq, d), what, f"out must be {(B, hq, d)}, got {tuple(out.shape)}")
     _same_device(what, q, k_cache, v_cache, out, cache_seqlens, block_table)
     lib = load_library()
-    _check(what, lib.attn_decode_paged_noalloc(
+    _check(what, _run(q.device, lib.attn_decode_paged_noalloc,
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _i32(cache_seqlens), _i32(block_table),
         B, hq, hkv, d, mbs, nb, bs, float(softmax_scale), int(split_tokens), _dt(q), _dt(out),
-        _stream(stream)))
+        _stream(q.device, stream)))
     return out
 
 
@@ -299,11 +310,11 @@ def attn_prefill_unfused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _same_device(what, q, k, v, out, cu_seqlens_q, cu_seqlens_k, workspace)
     lib = load_library()
-    _check("attn_prefill_unfused", lib.attn_prefill_unfused(
+    _check("attn_prefill_unfused", _run(q.device, lib.attn_prefill_unfused,
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _i32(cu_seqlens_q), _i32(cu_seqlens_k), B,
         int(max_seqlen_q), int(max_seqlen_k), total_q, total_k, hq, hkv, d, float(softmax_scale),
         int(bool(causal)), _dt(q), _dt(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _stream(stream)))
+        _stream(q.device, stream)))
     return out
 
 
@@ -326,7 +337,7 @@ def attn_prefill_padded(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seqle
     _need(tuple(out.shape) == (B, mq, hq, d), what, f"out must be {(B, mq, hq, d)}, got {tuple(out.shape)}")
     _same_device(what, q, k, v, out, seqlens_q, seqlens_k)
     lib = load_library()
-    _check("attn_prefill_padded", lib.attn_prefill_padded(
+    _check("attn_prefill_padded", _run(q.device, lib.attn_prefill_padded,
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _i32(seqlens_q), _i32(seqlens_k), B, mq, mk, hq, hkv, d,
-        float(softmax_scale), int(bool(causal)), _dt(q), _dt(out), _stream(stream)))
+        float(softmax_scale), int(bool(causal)), _dt(q), _dt(out), _stream(q.device, stream)))
     return out
