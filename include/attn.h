@@ -19,6 +19,9 @@
  *   host threads on different streams.
  * - stream is a hipStream_t passed as void* (NULL = the default stream).
  *   Calls are asynchronous on that stream and never synchronise the host.
+ *   Kernels launch on the current HIP device (hipSetDevice), whose compute
+ *   unit count sizes the persistent grids; the arrays and the stream must
+ *   belong to that device.
  * - Host-side argument validation runs before any HIP call.  On failure the
  *   call returns a nonzero status and launches nothing.  Launch failures
  *   return ATTN_ERR_HIP.  No C++ exception crosses the ABI.
