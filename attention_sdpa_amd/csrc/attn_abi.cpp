@@ -42,9 +42,11 @@ int resolve_split(int split) {
     return split > 0 ? split : 32;
 }
 
-// Decode workspace: partial slots (kDecodeMaxRuns + batch) x hq of d fp32
-// values; then (256-aligned) 2 fp32 words per slot and head (m, d'); then
-// (256-aligned) two int32 per sequence (its first and last run).
+// Decode workspace: partial slots (runs + batch) x hq of d fp32 values; then
+// (256-aligned) 2 fp32 words per slot and head (m, d'); then (256-aligned)
+// two int32 per sequence (its first and last run).  runs is kDecodeMaxRuns
+// for a caller's workspace (a size that holds on every device), the current
+// device's run count for the built-in scratch.
 struct DecodeLayout {
     int split;
     size_t ml_off;
@@ -52,12 +54,13 @@ struct DecodeLayout {
     size_t total;
 };
 
-bool decode_layout(int batch, int hq, int hkv, int d, int mbs, int bs, int split_req,
+bool decode_layout(int batch, int hq, int hkv, int d, int mbs, int bs, int split_req, int runs,
                    DecodeLayout *L) {
     if (batch <= 0 || hq <= 0 || hkv <= 0 || d <= 0 || mbs <= 0 || bs <= 0) return false;
     const int split = resolve_split(split_req);
     if (split <= 0) return false;
-    const size_t rows = ((size_t)attn::kDecodeMaxRuns + (size_t)batch) * (size_t)hq;
+    if (runs <= 0 || runs > attn::kDecodeMaxRuns) return false;
+    const size_t rows = ((size_t)runs + (size_t)batch) * (size_t)hq;
     L->split = split;
     L->ml_off = (rows * (size_t)d * sizeof(float) + 255) / 256 * 256;
     L->runs_off = (L->ml_off + rows * 2 * sizeof(float) + 255) / 256 * 256;
@@ -229,7 +232,7 @@ ATTN_API size_t attn_decode_workspace_bytes(int batch, int num_q_heads, int num_
                                             int block_size, int split_tokens) {
     DecodeLayout L;
     if (!decode_layout(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size,
-                       split_tokens, &L))
+                       split_tokens, attn::kDecodeMaxRuns, &L))
         return 0;
     return L.total;
 }
@@ -257,7 +260,7 @@ int decode_prepare(const void *q, const void *k_cache, const void *v_cache, void
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
         return ATTN_ERR_UNSUPPORTED;
     if (!decode_layout(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size,
-                       split_tokens, L))
+                       split_tokens, attn::kDecodeMaxRuns, L))
         return ATTN_ERR_SHAPE;
     if ((int64_t)max_blocks_per_seq * block_size > 0x7fffffffLL) return ATTN_ERR_SHAPE;
     if ((int64_t)batch * num_q_heads * head_dim > 0x7fffffffLL) return ATTN_ERR_SHAPE;
@@ -317,7 +320,21 @@ ATTN_API int attn_decode_paged_noalloc(const void *q, const void *k_cache, const
                                   num_kv_heads, head_dim, max_blocks_per_seq, num_blocks, block_size,
                                   softmax_scale, split_tokens, in_dtype, out_dtype, &a, &L);
     if (st != ATTN_OK) return st;
-    // the workspace this call needs must fit the per-device scratch array
+    // a one-run layout is the smallest any device needs: a call beyond the
+    // scratch even then is rejected before any HIP call
+    if (!decode_layout(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size,
+                       split_tokens, 1, &L) ||
+        L.total > attn::kDecodeScratchBytes)
+        return ATTN_ERR_WORKSPACE;
+    // the layout for the runs this device uses; it must fit the per-device
+    // scratch array
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return ATTN_ERR_HIP;
+    if (!decode_layout(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size,
+                       split_tokens, attn::decode_runs(num_kv_heads, cus), &L))
+        return ATTN_ERR_SHAPE;
     if (L.total > attn::kDecodeScratchBytes) return ATTN_ERR_WORKSPACE;
     void *ws = nullptr;
     if (attn::decode_scratch(&ws) != hipSuccess || ws == nullptr) return ATTN_ERR_HIP;

@@ -245,10 +245,12 @@ int attn_decode_paged(const void *q, const void *k_cache, const void *v_cache,
  * scratch array of 32 MiB built into the library, one per GPU, resolved on
  * the first call on each device and held until the process ends.
  *
- * Limit: the call must fit that scratch, i.e.
- * attn_decode_workspace_bytes(batch, ...) <= 32 MiB (at 32 query heads and
- * head_dim 128: batch <= 992); larger calls return ATTN_ERR_WORKSPACE and
- * launch nothing.  Nothing in the scratch needs clearing (every word the
+ * Limit: the call's workspace must fit that scratch.  It is laid out as in
+ * attn_decode_workspace_bytes but for the runs this device uses (its
+ * compute units divided by the blocks of up to 8 KV heads: 256 on a
+ * 256-CU MI355X with 8 KV heads) instead of the 1024 any device may use, so
+ * at head_dim 128 on that GPU: batch <= 1759 at 32 query heads, 752 at 64,
+ * 248 at 128.  Larger calls return ATTN_ERR_WORKSPACE and launch nothing.  Nothing in the scratch needs clearing (every word the
  * merge reads is written by the same call).  All calls on one GPU share its
  * scratch: calls that overlap in time on one GPU (different streams, or
  * host threads without ordering) race and give wrong results; serialise

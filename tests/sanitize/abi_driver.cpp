@@ -62,7 +62,7 @@ int main() {
                              need, nullptr), ATTN_ERR_UNSUPPORTED, "decode split");
     expect(attn_decode_paged(P, P, P, P, I, I, 4, 64, 2, 128, 32, 200, 256, 0.1f, 0, ATTN_BF16, ATTN_F32, P,
                              need, nullptr), ATTN_ERR_UNSUPPORTED, "decode group");
-    expect(attn_decode_paged_noalloc(P, P, P, P, I, I, 993, 32, 8, 128, 32, 200, 256, 0.1f, 0, ATTN_BF16,
+    expect(attn_decode_paged_noalloc(P, P, P, P, I, I, 2015, 32, 8, 128, 32, 200, 256, 0.1f, 0, ATTN_BF16,
                                      ATTN_F32, nullptr), ATTN_ERR_WORKSPACE, "decode noalloc beyond scratch");
     expect(attn_decode_paged_noalloc(P, P, P, P, I, I, 4, 32, 8, 128, 32, 200, 256, 0.f, 0, ATTN_BF16,
                                      ATTN_F32, nullptr), ATTN_ERR_SHAPE, "decode noalloc scale");

@@ -44,6 +44,21 @@ def test_noalloc_matches_workspace_entry_point_twice():
         check_bf16(np32(out), oracle_decode(dc), f"noalloc {name}")
 
 
+def test_noalloc_layout_follows_the_device_runs():
+    """The scratch layout counts the runs this device uses, not the 1024 a
+    caller's workspace is sized for: 64 query heads fit (their 1024-run
+    layout would not), and so do 1200 sequences at 32 heads (more than the
+    992 a 1024-run layout allows)."""
+    for name, dc in (("64 query heads", workloads.paged_decode(batch=6, lo=1, hi=900, hq=64, hkv=8,
+                                                               block_size=64, seed=331)),
+                     ("1200 sequences", workloads.paged_decode(batch=1200, lo=1, hi=40, hq=32, hkv=8,
+                                                               block_size=64, seed=332))):
+        log(f"case noalloc decode {name}")
+        ref_out, out = decode_pair(dc)
+        assert torch.equal(out, ref_out), f"{name}: differs from attn_decode_paged"
+        check_bf16(np32(out), oracle_decode(dc), f"noalloc {name}")
+
+
 def test_noalloc_rejects_calls_beyond_the_scratch():
     # 2048 sequences x 32 heads needs more than the 32 MiB scratch: rejected before any launch
     q = torch.zeros(2048, 32, 128, dtype=torch.bfloat16, device="cuda")
