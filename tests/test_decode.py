@@ -202,6 +202,15 @@ def test_decode_largest_item_size():
     check_bf16(np32(run_decode(dc, 2147483616)), oracle_decode(dc), "decode largest item size")
 
 
+def test_decode_long_context_128k():
+    """A 131072-token context beside short ones: a sequence spanning many
+    runs (the merge reads dozens of partials) and 512-entry block tables."""
+    dc = make_decode([131072, 5, 70000, 300], seed=73)
+    assert dc.paged.block_table.shape[1] == 512
+    log("case decode 128K context")
+    check_bf16(np32(run_decode(dc)), oracle_decode(dc), "decode 128K context")
+
+
 def test_decode_all_contexts_empty():
     """Every context length 0: the key stream has no item at all, no run is
     used, and every output row is 0."""
