@@ -175,6 +175,15 @@ def test_bf16_prefix_prefill_paged(block_size):
     check_bf16(np32(run_prefix(pp)), oracle_prefix(pp), f"prefix bs{block_size}")
 
 
+def test_bf16_prefix_long_context():
+    """New tokens on cached prefixes of 60K-100K tokens: units that stream
+    ~1,500 K/V tiles through the block table."""
+    pp = workloads.prefix_prefill(n_seqs=2, q_lo=1, q_hi=40, p_lo=60000, p_hi=100000, hq=32, hkv=8,
+                                  block_size=256, seed=27)
+    log("case bf16 prefix prefill, 60K-100K cached tokens")
+    check_bf16(np32(run_prefix(pp)), oracle_prefix(pp), "prefix long context")
+
+
 def test_bf16_shared_prefix_blocks():
     """Block tables that share their first physical blocks (one cached prompt
     read by every sequence; the page-table picture of the Prefill section has
