@@ -33,7 +33,10 @@
 //   ping-pong: while one group runs its matrix phase (the next tile's S^T and
 //   this tile's P V, MFMA after MFMA with LDS operand reads two steps
 //   ahead), the other computes a softmax on the vector ALUs; a workgroup
-//   barrier separates the half-steps.
+//   barrier separates the half-steps.  The last 6 of a matrix phase's 16
+//   P V MFMAs are issued at the start of the wave's next softmax phase,
+//   when its partner on the SIMD is issuing its tile loads and the matrix
+//   core would otherwise wait.
 // * K/V tiles reach LDS by direct global->LDS loads (global_load_lds_dwordx4,
 //   no register staging) into rings of three stages.  The group entering its
 //   matrix phase issues them (one group all K tiles, the other all V tiles),
@@ -652,6 +655,11 @@ prefill_mfma_kernel(VarlenArgs a, Geo geo) {
     float m_ref, mc_ref, l_run;
     f32x16 sacc[2];
     T8 pb[4];
+    // P V MFMAs of a step moved into the following softmax phase (measured
+    // best of 4..12: the partner wave's load issue leaves the matrix core
+    // idle for about that long), their V operands kept in registers
+    constexpr int kDefer = 6;
+    T8 vkeep[kDefer];
     // Q rows of unit u into qf.  A row past the sequence end reads the
     // sequence's first row instead: finite values confined to its own lane
     // pair, whose output is dropped.
@@ -755,8 +763,11 @@ prefill_mfma_kernel(VarlenArgs a, Geo geo) {
         // O^T += V^T P^T for the tile in V stage vs, with the row sums from
         // the same bf16 weights.  The two products alternate MFMA by MFMA;
         // the operands of step i + kAhead are read from LDS during step i.
-        auto mma = [&](int ks, int vs, auto with_qk) ATTN_INLINE {
+        // With defer, the last kDefer P V MFMAs only keep their V operands;
+        // the step loop issues them after the next barrier.
+        auto mma = [&](int ks, int vs, auto with_qk, auto defer) ATTN_INLINE {
             constexpr bool kQK = decltype(with_qk)::value;
+            constexpr bool kDef = decltype(defer)::value;
             constexpr int kAhead = 2;   // measured best of 1..5
             const bf16 *Kt = &sK[0][0] + ks * kTileElems;
             const bf16 *Vt = &sV[0][0] + vs * kTileElems;
@@ -795,7 +806,8 @@ prefill_mfma_kernel(VarlenArgs a, Geo geo) {
                     if (i + kAhead < 16) read_k(i + kAhead);
                 }
                 const int jj = i >> 2, db = i & 3;
-                o[db] = mfma_32x32x16(vbuf[i], pb[jj], o[db]);
+                if (kDef && i >= 16 - kDefer) vkeep[i - (16 - kDefer)] = vbuf[i];
+                else o[db] = mfma_32x32x16(vbuf[i], pb[jj], o[db]);
                 if (i + kAhead < 16) read_v(i + kAhead);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -908,11 +920,27 @@ prefill_mfma_kernel(VarlenArgs a, Geo geo) {
             issue();
             // every wave runs every step: past its last visible tile its P is
             // zero (adding exactly 0)
-            mma(st1, st, std::true_type{});
+            mma(st1, st, std::true_type{}, std::true_type{});
             __builtin_amdgcn_s_setprio(0);
             if (grpA) odd_barrier();
             else even_barrier();
+            // the deferred P V MFMAs (same operands, same order per
+            // accumulator: the same result bits), while the partner wavefront
+            // issues its loads, interleaved with the row sums of the same
+            // weights; both precede the softmax that overwrites pb and may
+            // rescale o
+#pragma unroll
+            for (int x = 0; x < kDefer; ++x) {
+                const int i = 16 - kDefer + x, jj = i >> 2, db = i & 3;
+                o[db] = mfma_32x32x16(vkeep[x], pb[jj], o[db]);
+            }
             sum_p();
+#pragma unroll
+            for (int x = 0; x < kDefer; ++x) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedValu, 16 / kDefer, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
             if (t + 1 < V.nw) softmax(t + 1);
             else zero_p();
             st = st1;
@@ -923,7 +951,7 @@ prefill_mfma_kernel(VarlenArgs a, Geo geo) {
             if (grpA) even_barrier();
             else odd_barrier();
             __builtin_amdgcn_s_setprio(1);
-            mma(st1, st, std::false_type{});
+            mma(st1, st, std::false_type{}, std::false_type{});   // nothing deferred: O is stored next
             __builtin_amdgcn_s_setprio(0);
             sum_p();
             Cn = find_unit(C.k + 1, false);
