@@ -41,6 +41,34 @@ def make_decode(ctx, hq=32, hkv=8, block_size=256, seed=0, mbs=None):
     return workloads.Decode(base.q.view(B, hq, 128), base.softmax_scale, pg, f"ctx{ctx}")
 
 
+@pytest.mark.parametrize("slope", [1.0, -1.0])
+@pytest.mark.parametrize("split", [0, 256])
+def test_decode_monotone_logits(slope, split):
+    """Logits rising (or falling) by ~1 per key along each context: rising,
+    every chunk raises the running maximum by ~32 and each run's partial
+    carries a maximum far above the previous run's, so the merge scales
+    all but the last runs' partials by factors that underflow to 0;
+    falling, the first chunk holds the maximum."""
+    ctx = [6000, 1, 777, 12000]
+    B, hq, hkv, d = len(ctx), 32, 8, 128
+    scale = d ** -0.5
+    g = torch.Generator().manual_seed(41)
+    T = sum(ctx)
+    q = torch.randn(B, hq, d, generator=g) * 0.5
+    k = torch.randn(T, hkv, d, generator=g) * 0.5
+    v = torch.randn(T, hkv, d, generator=g)
+    q[:, :, 0] = 16.0
+    pos = torch.cat([torch.arange(c, dtype=torch.float32) for c in ctx])
+    k[:, :, 0] = (pos * slope / (16.0 * scale))[:, None]
+    cu_k = torch.tensor([0] + list(np.cumsum(ctx)), dtype=torch.int32)
+    mbs = max((c + 255) // 256 for c in ctx)
+    pg = workloads.paged_pool(k.bfloat16(), v.bfloat16(), cu_k, [c - 1 for c in ctx], 256, 43,
+                              spare_blocks=2, max_blocks_per_seq=mbs)
+    dc = workloads.Decode(q.bfloat16(), scale, pg, "monotone logits")
+    log(f"case decode monotone logits slope={slope} split={split}")
+    check_bf16(np32(run_decode(dc, split)), oracle_decode(dc), f"decode slope {slope} split {split}")
+
+
 def test_decode_shapes_example():
     """The Decode section's example shapes: q [2, 32, 128] -> o [2, 32, 128]."""
     shp = load_golden("decode_shapes.txt")["q_shape"]

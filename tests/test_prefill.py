@@ -146,6 +146,37 @@ def test_bf16_one_hot_logits_exact():
     assert np.array_equal(got[:, 0], np.broadcast_to(np32(vl.v)[5, 0], (L, d)))
 
 
+def rising_logits(lens, hq, hkv, d, slope, seed):
+    """Packed bf16 q/k/v whose logits grow by about `slope` per key along
+    each sequence (feature 0 of every query is 16, of key j about
+    j * slope / (16 * scale)), plus N(0, 1/4) noise in the other features."""
+    scale = d ** -0.5
+    g = torch.Generator().manual_seed(seed)
+    T = sum(lens)
+    q = torch.randn(T, hq, d, generator=g) * 0.5
+    k = torch.randn(T, hkv, d, generator=g) * 0.5
+    v = torch.randn(T, hkv, d, generator=g)
+    q[:, :, 0] = 16.0
+    pos = torch.cat([torch.arange(L, dtype=torch.float32) for L in lens])
+    k[:, :, 0] = (pos * slope / (16.0 * scale))[:, None]
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32)
+    return q.bfloat16(), k.bfloat16(), v.bfloat16(), cu, scale
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_bf16_rising_logits_rescale_every_tile(causal):
+    """Logits rising by ~1 per key, 64 per 64-key tile: past the lazy
+    reference's threshold (a scaled rise of 8, 8 / (scale log2 e) ~ 63 logit
+    units at d = 128), so the reference and o', d' are rescaled on nearly
+    every tile, also while P V products of the step are still in flight."""
+    lens = [1000, 333, 700]
+    q, k, v, cu, scale = rising_logits(lens, 16, 4, 128, 1.0, 31)
+    vl = workloads.Varlen(q, k, v, cu, cu.clone(), max(lens), max(lens), scale, causal)
+    log(f"case bf16 rising logits causal={causal}")
+    got = np32(run_varlen(vl))
+    check_bf16(got, oracle_varlen(vl), f"rising logits causal={causal}")
+
+
 # ---------------------------------------------------------------- paged (prefix cache)
 
 def run_prefix(pp, out_dtype=torch.float32, store=True):
