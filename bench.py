@@ -575,9 +575,9 @@ def main():
                          "the reference for scaling the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the path shards by KV head or sequence with no exchange; see the design notes)",
-              file=sys.stderr)
+        print(f"bench.py: the benchmark runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the attention path would shard by KV head or by sequence, with no exchange "
+              "between GPUs)", file=sys.stderr)
         sys.exit(2)
 
     import torch
