@@ -12,7 +12,7 @@ import torch
 import attention_sdpa_amd as attn
 import oracle
 import workloads
-from tests.helpers import (check_bf16, check_bf16_output, check_f32, dev, log, np32,
+from tests.helpers import (check_bf16, check_bf16_output, check_f16, check_f32, dev, log, np32,
                            oracle_varlen, sample_rows, unit_rows)
 
 pytestmark = pytest.mark.gpu
@@ -146,7 +146,7 @@ def test_bf16_one_hot_logits_exact():
     assert np.array_equal(got[:, 0], np.broadcast_to(np32(vl.v)[5, 0], (L, d)))
 
 
-def rising_logits(lens, hq, hkv, d, slope, seed):
+def rising_logits(lens, hq, hkv, d, slope, seed, dtype=torch.bfloat16):
     """Packed bf16 q/k/v whose logits grow by about `slope` per key along
     each sequence (feature 0 of every query is 16, of key j about
     j * slope / (16 * scale)), plus N(0, 1/4) noise in the other features."""
@@ -160,7 +160,7 @@ def rising_logits(lens, hq, hkv, d, slope, seed):
     pos = torch.cat([torch.arange(L, dtype=torch.float32) for L in lens])
     k[:, :, 0] = (pos * slope / (16.0 * scale))[:, None]
     cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32)
-    return q.bfloat16(), k.bfloat16(), v.bfloat16(), cu, scale
+    return q.to(dtype), k.to(dtype), v.to(dtype), cu, scale
 
 
 @pytest.mark.parametrize("causal", [True, False])
@@ -175,6 +175,15 @@ def test_bf16_rising_logits_rescale_every_tile(causal):
     log(f"case bf16 rising logits causal={causal}")
     got = np32(run_varlen(vl))
     check_bf16(got, oracle_varlen(vl), f"rising logits causal={causal}")
+
+
+def test_f16_rising_logits_rescale_every_tile():
+    """The same rising logits with fp16 inputs (fp16 weights P, up to 2^8)."""
+    lens = [1000, 333, 700]
+    q, k, v, cu, scale = rising_logits(lens, 16, 4, 128, 1.0, 37, torch.float16)
+    vl = workloads.Varlen(q, k, v, cu, cu.clone(), max(lens), max(lens), scale, True)
+    log("case fp16 rising logits")
+    check_f16(np32(run_varlen(vl)), oracle_varlen(vl), "fp16 rising logits")
 
 
 # ---------------------------------------------------------------- paged (prefix cache)
